@@ -1,0 +1,327 @@
+// C ABI of the sparse FFN library: argument checks, weight packing,
+// workspace carving and the choice between the two execution paths.
+//
+//   token-gather path  fp32 layers, and bf16 batches of at most
+//                      kGatherMaxTokens tokens: only kept rows are read
+//   MFMA path          bf16 batches above that: dense-masked contraction on
+//                      the matrix cores (the union of many tokens' masks is
+//                      nearly every channel)
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/sparse_ffn.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kGatherMaxTokens = 4;
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+thread_local std::string g_last_error;
+
+sffn_status_t fail(sffn_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(sffn_dtype_t dt) { return dt == SFFN_BF16 ? 2 : 4; }
+
+sffn_status_t check_config(const sffn_config_t* c) {
+    if (!c) return fail(SFFN_ERR_INVALID_ARG, "config is null");
+    if (c->d <= 0 || c->d_i <= 0 || c->rank <= 0)
+        return fail(SFFN_ERR_INVALID_ARG, "d, d_i and rank must be positive (got %d, %d, %d)",
+                    c->d, c->d_i, c->rank);
+    if (c->bank != 64) return fail(SFFN_ERR_UNSUPPORTED, "bank must be 64 (got %d)", c->bank);
+    if (c->keep < 1 || c->keep > 64)
+        return fail(SFFN_ERR_INVALID_ARG, "keep must lie in [1, 64] (got %d)", c->keep);
+    if (c->d_i % 64 != 0 || c->d_i > 65536)
+        return fail(SFFN_ERR_INVALID_ARG, "d_i must be a multiple of 64 and <= 65536 (got %d)", c->d_i);
+    if (c->d % 64 != 0) return fail(SFFN_ERR_INVALID_ARG, "d must be a multiple of 64 (got %d)", c->d);
+    if (c->rank % 32 != 0)
+        return fail(SFFN_ERR_INVALID_ARG, "rank must be a multiple of 32 (got %d)", c->rank);
+    if (c->dtype != SFFN_F32 && c->dtype != SFFN_BF16)
+        return fail(SFFN_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
+    if (c->gate != SFFN_GATE_PREDICTOR && c->gate != SFFN_GATE_SILU)
+        return fail(SFFN_ERR_INVALID_ARG, "unknown gate %d", (int)c->gate);
+    return SFFN_OK;
+}
+
+struct PackedLayout {
+    size_t A, B, Wg, Wu, Wd, WdT, bias, total;
+};
+
+PackedLayout packed_layout(const sffn_config_t& c) {
+    const size_t e = elem_size(c.dtype);
+    const size_t d = (size_t)c.d, di = (size_t)c.d_i, r = (size_t)c.rank;
+    PackedLayout L{};
+    size_t off = 0;
+    L.A = off;    off += align_up(r * d * e);
+    L.B = off;    off += align_up(di * r * e);
+    L.Wg = off;   off += align_up(di * d * e);
+    L.Wu = off;   off += align_up(di * d * e);
+    L.Wd = off;   off += align_up(d * di * e);
+    L.WdT = off;  off += align_up(di * d * e);
+    L.bias = off; off += align_up(di * 4);
+    L.total = off;
+    return L;
+}
+
+bool use_gather(const sffn_config_t& c, int64_t T) {
+    return c.dtype == SFFN_F32 || T <= kGatherMaxTokens;
+}
+
+struct WsGather {
+    size_t z, ids, pk, h, partial, mask, logits, total;
+};
+struct WsMfma {
+    size_t z, logits, mask, h, total;
+};
+
+WsGather ws_gather(const sffn_config_t& c, int64_t T) {
+    const size_t nb = c.d_i / 64, ds = nb * c.keep;
+    const size_t groups = (size_t)sffn::gather_groups((int)ds);
+    WsGather w{};
+    size_t off = 0;
+    w.z = off;       off += align_up((size_t)T * c.rank * 4);
+    w.ids = off;     off += align_up((size_t)T * ds * 2);
+    w.pk = off;      off += align_up((size_t)T * ds * 4);
+    w.h = off;       off += align_up((size_t)T * ds * 4);
+    w.partial = off; off += align_up((size_t)T * groups * c.d * 4);
+    w.mask = off;    off += align_up((size_t)T * nb * 8);
+    w.logits = off;  // gather path writes logits only when asked
+    w.total = off;
+    return w;
+}
+
+WsMfma ws_mfma(const sffn_config_t& c, int64_t T) {
+    const size_t nb = c.d_i / 64;
+    WsMfma w{};
+    size_t off = 0;
+    w.z = off;      off += align_up((size_t)T * c.rank * 2);
+    w.logits = off; off += align_up((size_t)T * c.d_i * 4);
+    w.mask = off;   off += align_up((size_t)T * nb * 8);
+    w.h = off;      off += align_up((size_t)T * c.d_i * 2);
+    w.total = off;
+    return w;
+}
+
+sffn_status_t hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SFFN_OK;
+    return fail(SFFN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+template <typename P>
+P* at(void* base, size_t off) {
+    return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+struct sffn_layer {
+    sffn_config_t cfg;
+    void* packed;
+    PackedLayout L;
+    bool has_bias;
+    void* events[2 * sffn::kStages];
+    bool profiling;
+};
+
+extern "C" {
+
+size_t sparse_ffn_packed_size(const sffn_config_t* cfg) {
+    if (check_config(cfg) != SFFN_OK) return 0;
+    return packed_layout(*cfg).total;
+}
+
+sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* w_gate, const void* w_up,
+                                const void* w_down, const void* pred_a, const void* pred_b,
+                                const float* pred_bias, void* packed, size_t packed_bytes,
+                                void* hip_stream, sffn_handle_t* out) {
+    sffn_status_t st = check_config(cfg);
+    if (st != SFFN_OK) return st;
+    if (!out) return fail(SFFN_ERR_INVALID_ARG, "out is null");
+    const void* ptrs[] = {w_gate, w_up, w_down, pred_a, pred_b, packed};
+    const char* names[] = {"w_gate", "w_up", "w_down", "pred_a", "pred_b", "packed"};
+    for (int i = 0; i < 6; ++i) {
+        if (!ptrs[i]) return fail(SFFN_ERR_INVALID_ARG, "%s is null", names[i]);
+        if (!aligned16(ptrs[i])) return fail(SFFN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (pred_bias && !aligned16(pred_bias))
+        return fail(SFFN_ERR_INVALID_ARG, "pred_bias is not 16-byte aligned");
+    const PackedLayout L = packed_layout(*cfg);
+    if (packed_bytes < L.total)
+        return fail(SFFN_ERR_WORKSPACE, "packed buffer holds %zu bytes, %zu needed", packed_bytes, L.total);
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const size_t e = elem_size(cfg->dtype);
+    const size_t d = cfg->d, di = cfg->d_i, r = cfg->rank;
+    const sffn::Dt dt = cfg->dtype == SFFN_BF16 ? sffn::Dt::BF16 : sffn::Dt::F32;
+    hipError_t he = hipSuccess;
+    auto cp = [&](size_t off, const void* src, size_t bytes) {
+        if (he == hipSuccess) he = hipMemcpyAsync(at<char>(packed, off), src, bytes, hipMemcpyDeviceToDevice, s);
+    };
+    cp(L.A, pred_a, r * d * e);
+    cp(L.B, pred_b, di * r * e);
+    cp(L.Wg, w_gate, di * d * e);
+    cp(L.Wu, w_up, di * d * e);
+    cp(L.Wd, w_down, d * di * e);
+    if (pred_bias) cp(L.bias, pred_bias, di * 4);
+    if (he == hipSuccess) he = sffn::launch_transpose(dt, w_down, at<char>(packed, L.WdT), cfg->d, cfg->d_i, s);
+    if (he == hipSuccess) he = hipStreamSynchronize(s);
+    if (he != hipSuccess) return hip_status(he, "sparse_ffn_create");
+
+    sffn_layer* h = new (std::nothrow) sffn_layer;
+    if (!h) return fail(SFFN_ERR_INVALID_ARG, "out of host memory");
+    h->cfg = *cfg;
+    h->packed = packed;
+    h->L = L;
+    h->has_bias = pred_bias != nullptr;
+    h->profiling = false;
+    *out = h;
+    g_last_error.clear();
+    return SFFN_OK;
+}
+
+size_t sparse_ffn_workspace_size(sffn_handle_t h, int64_t T) {
+    if (!h || T <= 0) return 0;
+    return use_gather(h->cfg, T) ? ws_gather(h->cfg, T).total : ws_mfma(h->cfg, T).total;
+}
+
+sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void* y,
+                                 uint64_t* mask_out, float* logits_out, void* workspace,
+                                 size_t ws_bytes, void* hip_stream) {
+    if (!h) return fail(SFFN_ERR_INVALID_ARG, "handle is null");
+    if (T < 0) return fail(SFFN_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (T == 0) return SFFN_OK;
+    const sffn_config_t& c = h->cfg;
+    if (!x || !y) return fail(SFFN_ERR_INVALID_ARG, "x and y must not be null");
+    if (!aligned16(x) || !aligned16(y)) return fail(SFFN_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if (mask_out && !aligned16(mask_out)) return fail(SFFN_ERR_INVALID_ARG, "mask_out is not 16-byte aligned");
+    if (logits_out && !aligned16(logits_out))
+        return fail(SFFN_ERR_INVALID_ARG, "logits_out is not 16-byte aligned");
+    if (!workspace) return fail(SFFN_ERR_INVALID_ARG, "workspace is null");
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+        return fail(SFFN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    const int64_t nb = c.d_i / 64, ds = nb * c.keep;
+    // every launch's grid must fit in 31 bits
+    const int64_t biggest = T * (int64_t)c.d_i > T * ds * 2 ? T * (int64_t)c.d_i : T * ds * 2;
+    if (biggest / 4 >= kMaxGrid || T * nb * 8 >= kMaxGrid)
+        return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
+    const size_t need = sparse_ffn_workspace_size(h, T);
+    if (ws_bytes < need)
+        return fail(SFFN_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed for T = %lld", ws_bytes,
+                    need, (long long)T);
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const PackedLayout& L = h->L;
+    void* pk = h->packed;
+    const float* bias = h->has_bias ? at<float>(pk, L.bias) : nullptr;
+    hipError_t he;
+    if (use_gather(c, T)) {
+        const WsGather w = ws_gather(c, T);
+        sffn::GatherArgs a{};
+        a.dt = c.dtype == SFFN_BF16 ? sffn::Dt::BF16 : sffn::Dt::F32;
+        a.d = c.d; a.d_i = c.d_i; a.rank = c.rank; a.keep = c.keep; a.gate = (int)c.gate; a.T = T;
+        a.x = x; a.A = at<char>(pk, L.A); a.B = at<char>(pk, L.B); a.bias = bias;
+        a.W_g = at<char>(pk, L.Wg); a.W_u = at<char>(pk, L.Wu); a.W_dT = at<char>(pk, L.WdT);
+        a.y = y;
+        a.z = at<float>(workspace, w.z);
+        a.mask = mask_out ? mask_out : at<uint64_t>(workspace, w.mask);
+        a.logits = logits_out;
+        a.ids = at<uint16_t>(workspace, w.ids);
+        a.pk = at<float>(workspace, w.pk);
+        a.h = at<float>(workspace, w.h);
+        a.partial = at<float>(workspace, w.partial);
+        a.events = h->profiling ? h->events : nullptr;
+        he = sffn::launch_gather_forward(a, s);
+    } else {
+        const WsMfma w = ws_mfma(c, T);
+        sffn::MfmaArgs a{};
+        a.d = c.d; a.d_i = c.d_i; a.rank = c.rank; a.keep = c.keep; a.gate = (int)c.gate; a.T = T;
+        a.x = static_cast<const uint16_t*>(x);
+        a.A = at<const uint16_t>(pk, L.A); a.B = at<const uint16_t>(pk, L.B); a.bias = bias;
+        a.W_g = at<const uint16_t>(pk, L.Wg); a.W_u = at<const uint16_t>(pk, L.Wu);
+        a.W_d = at<const uint16_t>(pk, L.Wd);
+        a.y = static_cast<uint16_t*>(y);
+        a.z = at<uint16_t>(workspace, w.z);
+        a.logits = logits_out ? logits_out : at<float>(workspace, w.logits);
+        a.mask = mask_out ? mask_out : at<uint64_t>(workspace, w.mask);
+        a.h = at<uint16_t>(workspace, w.h);
+        a.events = h->profiling ? h->events : nullptr;
+        he = sffn::launch_mfma_forward(a, s);
+    }
+    return hip_status(he, "sparse_ffn_forward");
+}
+
+sffn_status_t bank_topk(const float* logits, int64_t T, int32_t d_i, int32_t keep,
+                        uint64_t* mask_out, uint16_t* idx_out, void* hip_stream) {
+    if (T < 0) return fail(SFFN_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (d_i <= 0 || d_i % 64 != 0 || d_i > 65536)
+        return fail(SFFN_ERR_INVALID_ARG, "d_i must be a positive multiple of 64, <= 65536 (got %d)", d_i);
+    if (keep < 1 || keep > 64) return fail(SFFN_ERR_INVALID_ARG, "keep must lie in [1, 64] (got %d)", keep);
+    if (T == 0) return SFFN_OK;
+    if (!logits || !mask_out) return fail(SFFN_ERR_INVALID_ARG, "logits and mask_out must not be null");
+    if (!aligned16(logits) || !aligned16(mask_out) || (idx_out && !aligned16(idx_out)))
+        return fail(SFFN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    if ((T * (d_i / 64) + 3) / 4 >= kMaxGrid)
+        return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
+    return hip_status(sffn::launch_bank_topk(logits, T, d_i, keep, mask_out, idx_out,
+                                             static_cast<hipStream_t>(hip_stream)),
+                      "bank_topk");
+}
+
+sffn_status_t sparse_ffn_set_stage_events(sffn_handle_t h, void* const* events, int32_t n_events) {
+    static_assert(sffn::kStages == SFFN_STAGES, "stage count");
+    if (!h) return fail(SFFN_ERR_INVALID_ARG, "handle is null");
+    if (!events) {
+        h->profiling = false;
+        return SFFN_OK;
+    }
+    if (n_events < 2 * sffn::kStages)
+        return fail(SFFN_ERR_INVALID_ARG, "%d events given, %d needed", n_events, 2 * sffn::kStages);
+    for (int i = 0; i < 2 * sffn::kStages; ++i) {
+        if (!events[i]) return fail(SFFN_ERR_INVALID_ARG, "event %d is null", i);
+        h->events[i] = events[i];
+    }
+    h->profiling = true;
+    return SFFN_OK;
+}
+
+const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
+    static const char* gather[] = {"pred1", "pred2_topk", "gateup", "down", "reduce"};
+    static const char* mfma[] = {"pred1_gemm", "pred2_gemm", "bank_topk", "gateup_gemm", "down_gemm"};
+    if (!h || i < 0 || i >= sffn::kStages) return nullptr;
+    return use_gather(h->cfg, T) ? gather[i] : mfma[i];
+}
+
+void sparse_ffn_destroy(sffn_handle_t h) { delete h; }
+
+const char* sparse_ffn_status_string(sffn_status_t s) {
+    switch (s) {
+        case SFFN_OK: return "ok";
+        case SFFN_ERR_INVALID_ARG: return "invalid argument";
+        case SFFN_ERR_UNSUPPORTED: return "unsupported";
+        case SFFN_ERR_WORKSPACE: return "buffer too small";
+        case SFFN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* sparse_ffn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

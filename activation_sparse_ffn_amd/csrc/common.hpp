@@ -1,0 +1,139 @@
+// Shared device helpers of the sparse FFN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sffn {
+
+constexpr int kWave = 64;
+constexpr int kBank = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN becomes the quiet NaN 0x7fc0.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// 8-element chunks: one 16-byte load for bf16, two for fp32
+// ---------------------------------------------------------------------------
+
+struct Chunk8 { float v[8]; };
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
+        uint4 w = *reinterpret_cast<const uint4*>(p);
+        o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x);
+        o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+        o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z);
+        o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+    }
+    static __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+template <> struct Elem<float> {
+    static __device__ __forceinline__ void load8(const float* p, float* o) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+    static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+};
+
+// Raw 16-byte words, loaded early and decoded later so that many loads are
+// in flight before the first use.
+template <typename T> struct Raw;
+template <> struct Raw<uint16_t> {
+    uint4 w;
+    __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void decode(float* o) const {
+        o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x);
+        o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+        o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z);
+        o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+    }
+};
+template <> struct Raw<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void decode(float* o) const {
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// wave reductions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float sigmoidf_dev(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// Order-preserving 32-bit key of a logit: larger value <=> larger key.
+// -0 and +0 share a key; every NaN gets key 0, below -inf (0x007fffff).
+__device__ __forceinline__ uint32_t rank_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+    if ((u & 0x7fffffffu) == 0u) return 0x80000000u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Bank-wise hard top-k of one 64-channel bank held one logit per lane.
+// Returns the wave-uniform mask of the `keep` largest keys, equal keys taken
+// lowest lane first. MSB-first radix search for the keep-th largest key,
+// stopping as soon as the candidate prefix isolates exactly `keep` lanes.
+__device__ __forceinline__ uint64_t wave_bank_topk(uint32_t key, int keep) {
+    if (keep >= kBank) return ~0ull;
+    uint32_t prefix = 0u;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = prefix | (1u << bit);
+        const uint64_t ge = __ballot(key >= cand);
+        const int c = __popcll(ge);
+        if (c >= keep) {
+            prefix = cand;
+            if (c == keep) return ge;
+        }
+    }
+    // prefix is now the keep-th largest key; split its ties by lane
+    const uint64_t gt = __ballot(key > prefix);
+    const uint64_t eq = __ballot(key == prefix);
+    const int need = keep - __popcll(gt);
+    const bool take = (key == prefix) && ((int)lanes_below(eq) < need);
+    return gt | __ballot(take);
+}
+
+}  // namespace sffn

@@ -1,0 +1,81 @@
+// Host-side launchers of the sparse FFN kernels. Each returns the
+// hipGetLastError() of its launches; callers have validated every argument.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sffn {
+
+enum class Dt { F32 = 0, BF16 = 1 };
+
+constexpr int kStages = 5;
+
+// Launches one stage's kernel. With profiling events attached, events[2i]
+// and events[2i+1] take the start and end timestamps of this kernel's own
+// dispatch (hipExtLaunchKernel), so host launch gaps are not counted.
+template <typename F, typename... Args>
+inline void xlaunch(void* const* events, int stage, F kernel, dim3 grid, dim3 block,
+                    uint32_t shmem, hipStream_t s, Args... args) {
+    hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[2 * stage]) : nullptr;
+    hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[2 * stage + 1]) : nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, args...);
+}
+
+// ---- bank top-k (one wave per (token, bank)) ------------------------------
+hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
+                            uint64_t* mask, uint16_t* ids, hipStream_t s,
+                            void* const* events = nullptr, int stage = 0);
+
+// ---- token-gather path (VALU; decode and fp32 layers) ---------------------
+struct GatherArgs {
+    Dt dt;
+    int d, d_i, rank, keep, gate;   // gate: 0 predictor, 1 silu
+    int64_t T;
+    const void* x;                  // [T, d]
+    const void* A;                  // [rank, d]
+    const void* B;                  // [d_i, rank]
+    const float* bias;              // [d_i] or null
+    const void* W_g;                // [d_i, d]
+    const void* W_u;                // [d_i, d]
+    const void* W_dT;               // [d_i, d] (W_d transposed)
+    void* y;                        // [T, d]
+    float* z;                       // [T, rank]       workspace
+    uint64_t* mask;                 // [T, d_i/64]
+    float* logits;                  // [T, d_i] or null
+    uint16_t* ids;                  // [T, d_s]        workspace
+    float* pk;                      // [T, d_s]        kept logits
+    float* h;                       // [T, d_s]        kept activations
+    float* partial;                 // [T, groups, d]  down partial sums
+    void* const* events;            // null or 2 * kStages hipEvent_t
+};
+int gather_groups(int d_s);
+hipError_t launch_gather_forward(const GatherArgs& a, hipStream_t s);
+
+// ---- dense-masked MFMA path (bf16, many tokens) ---------------------------
+struct MfmaArgs {
+    int d, d_i, rank, keep, gate;
+    int64_t T;
+    const uint16_t* x;      // [T, d]
+    const uint16_t* A;      // [rank, d]
+    const uint16_t* B;      // [d_i, rank]
+    const float* bias;      // [d_i] or null
+    const uint16_t* W_g;    // [d_i, d]
+    const uint16_t* W_u;    // [d_i, d]
+    const uint16_t* W_d;    // [d, d_i]
+    uint16_t* y;            // [T, d]
+    uint16_t* z;            // [T, rank]   workspace
+    float* logits;          // [T, d_i]
+    uint64_t* mask;         // [T, d_i/64]
+    uint16_t* h;            // [T, d_i]    workspace
+    void* const* events;    // null or 2 * kStages hipEvent_t
+};
+hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s);
+
+// ---- packing ---------------------------------------------------------------
+hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int cols,
+                            hipStream_t s);
+
+}  // namespace sffn

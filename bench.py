@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the predictor-gated bank-wise sparse SwiGLU FFN forward on
+one MI355X, with the CPU oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|batched|prefill]
+
+A step is one whole forward of the layer (predictor, bank top-k, gate/up on
+kept rows, down on kept columns) over one batch of synthetic tokens already
+resident in HBM:
+
+  decode   1 token per step (d = 4096, d_i = 14336, rank 448, 16 of 64 kept);
+           8 independently drawn layers are rotated and every step gets a
+           fresh token, so the ~105 MB a token touches are not served from
+           the 256 MB Infinity Cache. This is the default and the headline.
+  batched  32 tokens per step, predictor output bias b ~ N(0, 0.5).
+  prefill  4096 tokens per step with 1% outlier feature columns.
+
+The timed region replays a HIP graph of the steps (launch overhead removed).
+A second pass of the same steps launches each kernel with start/stop events
+(hipExtLaunchKernel) to get every stage's own duration; the dominant stage
+gives the roofline entry. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-FFN tokens/s per layer (d_i=14336) + achieved HBM GB/s / MFMA % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+WORKLOADS = {
+    "decode": dict(T=1, layers=8, bias=False, outliers=0.0),
+    "batched": dict(T=32, layers=8, bias=True, outliers=0.0),
+    "prefill": dict(T=4096, layers=2, bias=False, outliers=0.01),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle's bounded CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic(wl_name, shape, T, masks_union_frac=None):
+    """Algorithmic bytes and flops of one step.
+
+    Weights touched per token (bf16): predictor A and B in full, and for each
+    of the d_s kept channels one row of W_g, one of W_u and one of W_d^T.
+    """
+    d, d_i, r, ds = shape.d, shape.d_i, shape.rank, shape.d_s
+    e = 2
+    pred = (r * d + d_i * r) * e
+    row = d * e
+    if wl_name == "decode":
+        gateup = 2 * ds * row * T
+        down = ds * row * T
+        return dict(pred=pred * T, gateup=gateup, down=down, bytes=pred * T + gateup + down,
+                    flops=2 * T * (r * d + d_i * r + 3 * ds * d))
+    # batched / prefill: weights of the union of the batch's kept channels
+    u = masks_union_frac * d_i
+    gateup = int(2 * u * row)
+    down = int(u * row)
+    return dict(pred=pred, gateup=gateup, down=down, bytes=pred + gateup + down,
+                flops=2 * T * (r * d + d_i * r + 3 * ds * d),
+                executed_flops=2 * T * (r * d + d_i * r + 3 * d_i * d))
+
+
+def cpu_baseline(layer, T, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as o
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n_tok = 0
+    t0 = time.perf_counter()
+    seed = 1000
+    chunk = min(T, 4)
+    while time.perf_counter() - t0 < budget_s:
+        x = wl.make_tokens(layer.shape, chunk, seed=seed)
+        seed += 1
+        o.forward(x, layer.A, layer.B, layer.W_g, layer.W_u, layer.W_d, bias=layer.bias)
+        n_tok += chunk
+    el = time.perf_counter() - t0
+    return dict(value=n_tok / el, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{n_tok} tokens of the same layer in groups of {chunk}, "
+                       f"{el:.1f} s wall, float64 numpy oracle")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the layer would shard by tokens or by banks; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_amd as sffn
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = WORKLOADS[args.workload]
+    T = cfg["T"]
+    n_layers = args.layers or cfg["layers"]
+    shape = wl.FULL
+    K, W = args.steps, args.warmup
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    # ---- layers and tokens -------------------------------------------------
+    t0 = time.time()
+    ffns, layer0 = [], None
+    for li in range(n_layers):
+        L = wl.make_layer(shape, seed=li, bias_var=0.5 if cfg["bias"] else None)
+        ffns.append(sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B),
+                                   dev(L.bias) if cfg["bias"] else None))
+        if li == 0:
+            layer0 = L
+        del L
+        torch.cuda.empty_cache()
+    n_x = 64 if T == 1 else (16 if T <= 32 else 2)
+    xs = [dev(wl.make_tokens(shape, T, seed=10_000 + i, outlier_frac=cfg["outliers"]))
+          for i in range(n_x)]
+    ys = [torch.empty_like(x) for x in xs]
+    ws = torch.empty(ffns[0].workspace_size(T), dtype=torch.uint8, device="cuda")
+    masks = [torch.empty((T, shape.n_banks), dtype=torch.int64, device="cuda") for _ in range(n_x)]
+    log(f"setup {time.time() - t0:.1f}s: {n_layers} layers, {n_x} token batches of T={T}")
+
+    G = n_x * n_layers // np.gcd(n_x, n_layers)     # steps per graph: every (x, layer) pair once
+    G = min(G, 64)
+
+    def step(i):
+        j = i % n_x
+        ffns[i % n_layers](xs[j], y=ys[j], mask=masks[j], workspace=ws)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(G):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        # the graph reproduces eager results bit for bit
+        y_graph = [y.clone() for y in ys]
+        with torch.cuda.stream(stream):
+            for i in range(G):
+                step(i)
+        torch.cuda.synchronize()
+        for a, b in zip(y_graph, ys):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
+
+    # ---- timed region -------------------------------------------------------
+    reps, rem = divmod(K, G) if graph is not None else (0, K)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        for i in range(rem):
+            step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / K
+    tokens_per_s = T * K / (ms / 1e3)
+    log(f"timed {K} steps: {ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.1f} tokens/s")
+
+    # ---- union of kept channels (batched / prefill bytes) -------------------
+    union_frac = None
+    if T > 1:
+        fr = []
+        for m in masks:
+            w = m.cpu().numpy().view(np.uint64)
+            fr.append(np.bitwise_count(np.bitwise_or.reduce(w, axis=0)).sum() / shape.d_i)
+        union_frac = float(np.mean(fr))
+    alg = algorithmic(args.workload, shape, T, union_frac)
+
+    # ---- per-stage durations (kernel start/stop events) ---------------------
+    n_ev = 2 * sffn.SFFN_STAGES
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    with torch.cuda.stream(stream):
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for f in ffns:
+        f.set_stage_events([e.cuda_event for e in evs])
+    stage_ms = np.zeros(sffn.SFFN_STAGES)
+    n_prof = min(K, 256)
+    with torch.cuda.stream(stream):
+        for i in range(n_prof):
+            step(i)
+            stream.synchronize()
+            stage_ms += [evs[2 * s].elapsed_time(evs[2 * s + 1]) for s in range(sffn.SFFN_STAGES)]
+    for f in ffns:
+        f.set_stage_events(None)
+    stage_us = stage_ms / n_prof * 1e3
+    names = ffns[0].stage_names(T)
+    stages = {n: round(float(u), 3) for n, u in zip(names, stage_us)}
+    log(f"stages (us): {stages}")
+
+    # ---- roofline of the dominant kernel ------------------------------------
+    if args.workload == "decode":
+        dom = "gateup"
+        dur_s = stage_us[names.index(dom)] * 1e-6
+        achieved = alg["gateup"] / dur_s / 1e9
+        roof = dict(kernel="k_gateup", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    bytes_per_launch=alg["gateup"], avg_us=round(float(stage_us[names.index(dom)]), 3))
+    else:
+        dom = "gateup_gemm"
+        dur_s = stage_us[names.index(dom)] * 1e-6
+        fl = 2 * T * 2 * shape.d_i * shape.d        # executed: dense gate and up
+        achieved = fl / dur_s / 1e12
+        roof = dict(kernel="k_gemm<EPI_GATEUP>", bound="mfma", achieved=round(achieved, 1),
+                    peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4),
+                    traffic=None, flops_per_launch=fl,
+                    avg_us=round(float(stage_us[names.index(dom)]), 3))
+        if args.workload == "batched":
+            # a T = 32 batch is bound by streaming the union's weight rows
+            gb = alg["gateup"] / dur_s / 1e9
+            roof.update(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(gb / HBM_PEAK_GBS, 4), bytes_per_launch=alg["gateup"])
+            roof.pop("flops_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 1/fan_in) weights, N(0, 1) tokens)",
+        "config": {
+            "workload": f"{args.workload}: {T} token(s) per step, d=4096, d_i=14336, rank=448, "
+                        f"keep 16 of 64 per bank, {n_layers} layers rotated",
+            "tokens_per_step": T, "layers_rotated": n_layers, "graph": graph is not None,
+        },
+        "step_hbm_gbs": round(alg["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_algorithmic_bytes": alg["bytes"],
+        "stages_us": stages,
+        "roofline": roof,
+    }
+    if union_frac is not None:
+        out["union_frac"] = round(union_frac, 4)
+        out["executed_tflops"] = round(alg["executed_flops"] / (ms_per_step * 1e-3) / 1e12, 1)
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(layer0, T, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,369 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (the layer's correctness criteria):
+* bank top-k masks are bit-exact when both sides get the same fp32 logits;
+* end-to-end, a (token, bank) mask may differ from the oracle's only where
+  the oracle's keep-th / (keep+1)-th logit gap is below 1e-3;
+* y is within relative L2 2e-2 of the oracle, per token with the GPU's mask
+  pinned into the oracle, and over the whole tensor end to end.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+import workloads as wl
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+REL_L2 = 2e-2
+GAP = 1e-3
+
+
+def dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def words(t):
+    return t.cpu().numpy().view(np.uint64)
+
+
+def make_ffn(layer, bias=True, keep=16, gate="pred"):
+    import activation_sparse_ffn_amd as sffn
+    L = layer
+    return sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B),
+                          dev(L.bias) if (bias and L.bias is not None) else None,
+                          keep=keep, gate=gate)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_forward(layer, x, y, mask, logits, tokens=None, bias=True, keep=16, gate="pred"):
+    """Compare one GPU forward with the oracle on the chosen token rows."""
+    L = layer
+    b = L.bias if bias else None
+    T = x.shape[0]
+    rows = np.arange(T) if tokens is None else np.asarray(tokens)
+    gw = words(mask)
+    gl = host(logits)
+    yg = o.widen(host(y))
+    # 1. the GPU's own logits give the GPU's mask (bit-exact top-k)
+    np.testing.assert_array_equal(o.mask_to_words(o.bank_topk_mask(gl[rows], 64, keep)), gw[rows])
+    assert (np.bitwise_count(gw[rows]) == keep).all()
+    # 2. end-to-end masks differ only where the oracle's logit gap is tiny
+    r = o.forward(x, L.A, L.B, L.W_g, L.W_u, L.W_d, bias=b, keep=keep, gate=gate, tokens=rows)
+    gap = o.logit_gap(r["p"], 64, keep)
+    diff = gw[rows] != r["words"]
+    assert (gap[diff] < GAP).all(), f"mask differs with gap {gap[diff].max()}"
+    # the logits themselves agree closely (fp32 accumulation vs float64)
+    scale = np.abs(r["p"]).max()
+    assert np.abs(gl[rows].astype(np.float64) - r["p"]).max() <= 2e-3 * max(scale, 1.0)
+    # 3. y per token with the GPU's mask pinned into the oracle
+    y_pin = r["y"].copy()
+    bad = np.flatnonzero(diff.any(axis=1))
+    if len(bad):
+        rp = o.forward(x, L.A, L.B, L.W_g, L.W_u, L.W_d, bias=b, keep=keep, gate=gate,
+                       mask_in=gw, tokens=rows[bad])
+        y_pin[bad] = rp["y"]
+    for n, t in enumerate(rows):
+        e = rel_l2(yg[t], y_pin[n])
+        assert e <= REL_L2, f"token {t}: rel-L2 {e:.3e} (mask pinned)"
+    # 4. end to end over the whole tensor
+    assert rel_l2(yg[rows], r["y"]) <= REL_L2
+    return r, int(diff.sum())
+
+
+# ---------------------------------------------------------------------------
+# fixtures
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def full_layer():
+    return wl.make_layer(wl.FULL, seed=0, bias_var=0.5)
+
+
+@pytest.fixture(scope="module")
+def ffn_full(full_layer):
+    return make_ffn(full_layer, bias=False)
+
+
+@pytest.fixture(scope="module")
+def ffn_full_bias(full_layer):
+    return make_ffn(full_layer, bias=True)
+
+
+MID = wl.LayerShape(d=512, d_i=2048, rank=64)
+
+
+@pytest.fixture(scope="module")
+def mid_layer():
+    return wl.make_layer(MID, seed=4, bias_var=0.5)
+
+
+# ---------------------------------------------------------------------------
+# bank top-k alone
+# ---------------------------------------------------------------------------
+
+def _specials(T=6, d_i=256):
+    rng = np.random.default_rng(11)
+    p = rng.standard_normal((T, d_i)).astype(np.float32)
+    p[0, :64] = np.nan
+    p[1, :64:3] = np.inf
+    p[1, 1:64:3] = -np.inf
+    p[2, :64] = np.where(np.arange(64) % 2, -0.0, 0.0)
+    p[3, 64:128] = 1.0
+    p[4, 5:60] = np.nan
+    p[5, 128:192] = np.arange(64, dtype=np.float32)[::-1]
+    p[5, 192:256] = np.float32(1e-45) * (np.arange(64) % 3 - 1)   # subnormals and zeros
+    return p
+
+
+@pytest.mark.parametrize("keep", [1, 7, 16, 48, 63, 64])
+def test_bank_topk_bit_exact(keep):
+    import activation_sparse_ffn_amd as sffn
+    cases = [np.random.default_rng(1).standard_normal((37, 1024)).astype(np.float32),
+             wl.make_tie_logits(T=29, d_i=2048, seed=5),
+             wl.make_stress_logits(T=13, d_i=14336, seed=6),
+             _specials()]
+    for p in cases:
+        mask, ids = sffn.bank_topk(dev(p), keep=keep, return_ids=True)
+        torch.cuda.synchronize()
+        m = o.bank_topk_mask(p, 64, keep)
+        np.testing.assert_array_equal(words(mask), o.mask_to_words(m))
+        ids_np = ids.cpu().numpy().view(np.uint16)
+        for t in range(p.shape[0]):
+            np.testing.assert_array_equal(ids_np[t], np.flatnonzero(m[t]))
+
+
+def test_bank_topk_stress_full_size():
+    """32768 x 14336 fp32 logits with 5% exact ties per bank: the oracle on a
+    seeded sample of tokens, structural properties on every bank."""
+    import activation_sparse_ffn_amd as sffn
+    cfg = wl.CONFIGS["topk_stress"]
+    p = wl.make_stress_logits(T=cfg["T"], d_i=cfg["d_i"], seed=0, tie_frac=cfg["tie_frac"])
+    pd = dev(p)
+    mask, ids = sffn.bank_topk(pd, keep=16, return_ids=True)
+    torch.cuda.synchronize()
+    w = words(mask)
+    assert w.shape == (32768, 224)
+    assert (np.bitwise_count(w) == 16).all()
+    sample = np.sort(np.random.default_rng(0).choice(32768, size=96, replace=False))
+    sample = np.concatenate([[0], sample, [32767]])
+    np.testing.assert_array_equal(w[sample], o.mask_to_words(o.bank_topk_mask(p[sample], 64, 16)))
+    # every kept logit >= every dropped logit of its bank, on the GPU
+    bits = (mask.unsqueeze(-1) >> torch.arange(64, device="cuda")) & 1
+    v = pd.view(32768, 224, 64)
+    kmin = torch.where(bits.bool(), v, torch.full_like(v, float("inf"))).amin(-1)
+    dmax = torch.where(bits.bool(), torch.full_like(v, float("-inf")), v).amax(-1)
+    assert bool((kmin >= dmax).all())
+    # on ties at the boundary the lower channel wins: a dropped value equal to
+    # the smallest kept value must sit above every kept channel holding it
+    tie = (dmax == kmin)
+    assert int(tie.sum()) > 0
+    idx = torch.arange(64, device="cuda").expand_as(v)
+    at_kmin = v == kmin.unsqueeze(-1)
+    last_kept = torch.where(bits.bool() & at_kmin, idx, torch.full_like(idx, -1)).amax(-1)
+    first_dropped = torch.where(~bits.bool() & at_kmin, idx, torch.full_like(idx, 99)).amin(-1)
+    assert bool((last_kept[tie] < first_dropped[tie]).all())
+    ids_np = ids.cpu().numpy().view(np.uint16)
+    for t in sample[:8]:
+        np.testing.assert_array_equal(ids_np[t], np.flatnonzero(o.words_to_mask(w[t:t + 1])[0]))
+
+
+# ---------------------------------------------------------------------------
+# whole forward
+# ---------------------------------------------------------------------------
+
+def test_forward_tiny_fp32():
+    layer = wl.make_layer(wl.TINY, seed=0)
+    ffn = make_ffn(layer)
+    for T in (8, 1, 3):
+        x = wl.make_tokens(wl.TINY, T, seed=T)
+        y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+        torch.cuda.synchronize()
+        r, ndiff = check_forward(layer, x, y, mask, logits)
+        assert ndiff == 0
+        assert rel_l2(o.widen(host(y)), r["y"]) < 1e-5      # fp32 layer: fp32-level agreement
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_forward_decode_full(full_layer, ffn_full, T):
+    x = wl.make_tokens(wl.FULL, T, seed=100 + T)
+    y, mask, logits = ffn_full(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(full_layer, x, y, mask, logits, bias=False)
+
+
+def test_forward_batched_full(full_layer, ffn_full_bias):
+    x = wl.make_tokens(wl.FULL, 32, seed=200)
+    y, mask, logits = ffn_full_bias(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(full_layer, x, y, mask, logits, bias=True)
+    union = np.bitwise_or.reduce(words(mask), axis=0)
+    frac = np.bitwise_count(union).sum() / 14336
+    assert 0.5 < frac < 1.0      # partial overlap across tokens
+
+
+@pytest.mark.parametrize("T", [5, 130])
+def test_forward_mfma_ragged_full(full_layer, ffn_full, T):
+    x = wl.make_tokens(wl.FULL, T, seed=300 + T)
+    y, mask, logits = ffn_full(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    rows = None if T <= 8 else [0, 1, 63, 64, 127, 128, 129]
+    check_forward(full_layer, x, y, mask, logits, tokens=rows, bias=False)
+
+
+def test_forward_prefill_chunk(full_layer, ffn_full):
+    cfg = wl.CONFIGS["prefill"]
+    x = wl.make_tokens(wl.FULL, cfg["T"], seed=0, outlier_frac=cfg["outlier_frac"])
+    y, mask, logits = ffn_full(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    rows = np.concatenate([[0, 127, 128, 4095],
+                           np.random.default_rng(1).choice(4096, size=8, replace=False)])
+    check_forward(full_layer, x, y, mask, logits, tokens=rows, bias=False)
+    assert (np.bitwise_count(words(mask)) == 16).all()
+
+
+def test_forward_long_context_chunks(full_layer, ffn_full):
+    """32768 tokens through one handle in 8 chunks of 4096: sampled tokens of
+    every chunk against the oracle, and chunking does not change any row."""
+    cfg = wl.CONFIGS["longctx"]
+    T, C = cfg["T"], cfg["chunk"]
+    x = wl.make_tokens(wl.FULL, T, seed=7, outlier_frac=cfg["outlier_frac"])
+    xd = dev(x)
+    ys, masks, logits = [], [], []
+    for c in range(T // C):
+        y, m, lg = ffn_full(xd[c * C:(c + 1) * C], return_mask=True, return_logits=True)
+        ys.append(y.clone()); masks.append(m.clone()); logits.append(lg.clone())
+    y = torch.cat(ys); mask = torch.cat(masks); lg = torch.cat(logits)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = np.sort(np.concatenate([c * C + rng.choice(C, size=2, replace=False) for c in range(T // C)]))
+    check_forward(full_layer, x, y, mask, lg, tokens=rows, bias=False)
+    # the same tokens in one 4096-row call at another offset give identical rows
+    y2 = ffn_full(xd[C // 2:C // 2 + C])
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y[C // 2:C // 2 + C].view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 64, 200])
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_forward_mid_shapes(mid_layer, T, gate):
+    ffn = make_ffn(mid_layer, bias=True, gate=gate)
+    x = wl.make_tokens(MID, T, seed=T)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(mid_layer, x, y, mask, logits, bias=True, gate=gate)
+
+
+@pytest.mark.parametrize("T", [2, 16])
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_keep_all_channels_is_dense(mid_layer, T, gate):
+    """keep = 64: the predictor-gated dense FFN (every channel kept)."""
+    ffn = make_ffn(mid_layer, bias=True, keep=64, gate=gate)
+    x = wl.make_tokens(MID, T, seed=50 + T)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    assert (words(mask) == np.uint64(2**64 - 1)).all()
+    check_forward(mid_layer, x, y, mask, logits, bias=True, keep=64, gate=gate)
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_gate_silu_full(full_layer, T):
+    ffn = make_ffn(full_layer, bias=True, gate="silu")
+    x = wl.make_tokens(wl.FULL, T, seed=400 + T)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(full_layer, x, y, mask, logits, bias=True, gate="silu")
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_poisoned_skipped_weights(mid_layer, T):
+    """Inactive channels are exactly zero: NaN in every weight row the batch
+    does not keep leaves y bit-identical (W_d columns get large finite values
+    on the dense MFMA path, where a skipped column still meets an exact 0)."""
+    L = mid_layer
+    x = dev(wl.make_tokens(MID, T, seed=60 + T))
+    ffn = make_ffn(L)
+    y0, mask = ffn(x, return_mask=True)
+    torch.cuda.synchronize()
+    union = o.words_to_mask(np.bitwise_or.reduce(words(mask), axis=0)[None])[0]
+    dead = ~union
+    assert dead.any()
+    Wg, Wu, Wd = (o.widen(w).astype(np.float32) for w in (L.W_g, L.W_u, L.W_d))
+    Wg[dead] = np.nan
+    Wu[dead] = np.nan
+    Wd[:, dead] = np.nan if T <= 4 else 3.0e38
+    to_bf = wl.bf16_bits_from_f32
+    poisoned = wl.Layer(L.shape, L.A, L.B, to_bf(Wg), to_bf(Wu), to_bf(Wd), L.bias)
+    y1 = make_ffn(poisoned)(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert bool(torch.isfinite(y1.float()).all())
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_deterministic_and_power_of_two_scaling(mid_layer, T):
+    L = mid_layer
+    x = dev(wl.make_tokens(MID, T, seed=70 + T))
+    ffn = make_ffn(L)
+    y0 = ffn(x).clone()
+    y1 = ffn(x).clone()
+    Wu2 = wl.bf16_bits_from_f32(2 * o.widen(L.W_u).astype(np.float32))
+    y2 = make_ffn(wl.Layer(L.shape, L.A, L.B, L.W_g, Wu2, L.W_d, L.bias))(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal((2 * y0.float()).view(torch.int32), y2.float().view(torch.int32))
+
+
+def test_errors_reported_through_the_abi(mid_layer):
+    import activation_sparse_ffn_amd as sffn
+    ffn = make_ffn(mid_layer)
+    x = dev(wl.make_tokens(MID, 4, seed=1))
+    need = ffn.workspace_size(4)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sffn.SparseFFNError) as e:
+        ffn(x, workspace=small)
+    assert e.value.status == sffn.SFFN_ERR_WORKSPACE
+    lib = sffn.load_library()
+    y = torch.empty_like(x)
+    ws = ffn.workspace(4)
+    st = lib.sparse_ffn_forward(ffn._h, ctypes.c_void_p(x.data_ptr() + 2), 4, ctypes.c_void_p(y.data_ptr()),
+                                None, None, ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert st == sffn.SFFN_ERR_INVALID_ARG
+    assert ffn(x[:0]).shape == (0, MID.d)     # T = 0 is a no-op
+
+
+def test_stage_events_time_every_stage(mid_layer):
+    ffn = make_ffn(mid_layer)
+    x = dev(wl.make_tokens(MID, 1, seed=1))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+    for e in evs:
+        e.record()          # materialise the underlying hipEvent_t
+    torch.cuda.synchronize()
+    ffn.set_stage_events([e.cuda_event for e in evs])
+    ffn(x)
+    torch.cuda.synchronize()
+    ts = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(5)]
+    assert all(0 < t < 100 for t in ts), ts
+    assert ffn.stage_names(1)[2] == "gateup" and ffn.stage_names(64)[3] == "gateup_gemm"
+    ffn.set_stage_events(None)

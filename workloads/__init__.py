@@ -145,8 +145,9 @@ def make_stress_logits(T: int, d_i: int, seed: int = 0, bank: int = 64,
                        tie_frac: float = 0.05) -> np.ndarray:
     """fp32 logits [T, d_i] ~ N(0, 1) with exact ties injected per bank.
 
-    In every bank, round(tie_frac * bank) positions are overwritten with the
-    value of another, randomly chosen position of the same bank.
+    In every bank, round(tie_frac * bank) positions are overwritten, each with
+    the value of a randomly chosen position of the same bank that is not
+    overwritten, so every bank holds at least one exact tie.
     """
     r = _rngs(seed)
     p = r["x"].standard_normal(size=(T, d_i), dtype=np.float32)
@@ -155,9 +156,19 @@ def make_stress_logits(T: int, d_i: int, seed: int = 0, bank: int = 64,
         nb = d_i // bank
         pv = p.reshape(T, nb, bank)
         g = r["spare"]
-        # destinations: n_tie distinct positions per bank; sources: any other position
-        dst = np.argsort(g.random((T, nb, bank), dtype=np.float32), axis=-1)[..., :n_tie]
-        src = (dst + 1 + g.integers(0, bank - 1, size=dst.shape)) % bank
+        def skip_taken(pick, taken):
+            # map pick in [0, bank - n) to the pick-th position not in `taken`
+            for col in np.split(np.sort(taken, axis=-1), taken.shape[-1], axis=-1):
+                pick += pick >= col
+            return pick
+
+        # destinations: n_tie distinct positions per bank, one at a time
+        dst = g.integers(0, bank, size=(T, nb, 1))
+        for k in range(1, n_tie):
+            dst = np.concatenate([dst, skip_taken(g.integers(0, bank - k, size=(T, nb, 1)), dst)],
+                                 axis=-1)
+        # sources: positions that are not destinations
+        src = skip_taken(g.integers(0, bank - n_tie, size=dst.shape), dst)
         vals = np.take_along_axis(pv, src, axis=-1)
         np.put_along_axis(pv, dst, vals, axis=-1)
     return p
