@@ -10,6 +10,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -94,7 +95,9 @@ struct WsMfma {
 
 WsGather ws_gather(const sffn_config_t& c, int64_t T) {
     const size_t nb = c.d_i / 64, ds = nb * c.keep;
-    const size_t groups = (size_t)sffn::gather_groups((int)ds);
+    // partial rows of y: one per group of 64 kept channels (generic path) or
+    // one per bank (fused path); the larger count covers both
+    const size_t groups = std::max((size_t)sffn::gather_groups((int)ds), nb);
     WsGather w{};
     size_t off = 0;
     w.z = off;       off += align_up((size_t)T * c.rank * 4);
@@ -304,9 +307,14 @@ sffn_status_t sparse_ffn_set_stage_events(sffn_handle_t h, void* const* events, 
 
 const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
     static const char* gather[] = {"pred1", "pred2_topk", "gateup", "down", "reduce"};
+    static const char* fused[] = {"pred1", "bank_fused", "reduce", "none", "none"};
     static const char* mfma[] = {"pred1_gemm", "pred2_gemm", "bank_topk", "gateup_gemm", "down_gemm"};
     if (!h || i < 0 || i >= sffn::kStages) return nullptr;
-    return use_gather(h->cfg, T) ? gather[i] : mfma[i];
+    if (!use_gather(h->cfg, T)) return mfma[i];
+    sffn::GatherArgs a{};
+    a.dt = h->cfg.dtype == SFFN_BF16 ? sffn::Dt::BF16 : sffn::Dt::F32;
+    a.d = h->cfg.d; a.d_i = h->cfg.d_i; a.rank = h->cfg.rank; a.keep = h->cfg.keep;
+    return sffn::fused_ok(a) ? fused[i] : gather[i];
 }
 
 void sparse_ffn_destroy(sffn_handle_t h) { delete h; }

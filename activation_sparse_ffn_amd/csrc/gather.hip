@@ -17,32 +17,33 @@
 namespace sffn {
 
 // ---------------------------------------------------------------------------
-// predictor layer 1: one wave per (token, rank row)
+// predictor layer 1: one workgroup per (token, rank row); the four waves split
+// the d-long dot product and meet in LDS. EXACT: d/8 is a multiple of 256*NC.
 // ---------------------------------------------------------------------------
-template <typename E, int NC>
+template <typename E, int NC, bool EXACT>
 __global__ __launch_bounds__(256) void k_pred1(const E* __restrict__ x, const E* __restrict__ A,
                                                float* __restrict__ z, int d, int rank,
-                                               int64_t n_work, int round_bf16) {
-    const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= n_work) return;
-    const int64_t t = w / rank;
-    const int q = (int)(w - t * rank);
-    const E* xr = x + t * d;
-    const E* ar = A + (int64_t)q * d;
+                                               int round_bf16) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const unsigned w = blockIdx.x;
+    const unsigned t = w / (unsigned)rank;
+    const unsigned q = w - t * (unsigned)rank;
+    const E* xr = x + (size_t)t * d;
+    const E* ar = A + (size_t)q * d;
     const int nch = d / 8;
     float acc = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 64 * NC) {
+    for (int c0 = 0; c0 < nch; c0 += 256 * NC) {
         Raw<E> rx[NC], ra[NC];
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            const int c = c0 + lane + 64 * k;
-            if (c < nch) { rx[k].load(xr + 8 * c); ra[k].load(ar + 8 * c); }
+            const int c = c0 + tid + 256 * k;
+            if (EXACT || c < nch) { ra[k].load(ar + 8 * c); rx[k].load(xr + 8 * c); }
         }
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
-            const int c = c0 + lane + 64 * k;
-            if (c < nch) {
+            const int c = c0 + tid + 256 * k;
+            if (EXACT || c < nch) {
                 float xv[8], av[8];
                 rx[k].decode(xv);
                 ra[k].decode(av);
@@ -52,24 +53,36 @@ __global__ __launch_bounds__(256) void k_pred1(const E* __restrict__ x, const E*
         }
     }
     acc = wave_sum(acc);
-    if (lane == 0) z[w] = round_bf16 ? bf16_to_f32(f32_to_bf16(acc)) : acc;
+    if (lane == 0) red[wv] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        const float v = (red[0] + red[1]) + (red[2] + red[3]);
+        z[w] = round_bf16 ? bf16_to_f32(f32_to_bf16(v)) : v;
+    }
 }
 
-// Sixteen per-lane partial sums -> full wave sums. On return every lane
-// holds the sum of row (lane >> 2) in r[0].
-__device__ __forceinline__ void reduce16_rows(float (&r)[16], int lane) {
+// N per-lane partial sums (N a power of two) -> full wave sums. Each
+// butterfly step trades half of the rows with the partner lane, so the whole
+// reduction costs N - 1 + (6 - log2 N) shuffles. On return every lane holds
+// the sum of row (lane >> (6 - log2 N)) in r[0].
+template <int N>
+__device__ __forceinline__ void reduce_rows(float (&r)[N], int lane) {
+    constexpr int L = __builtin_ctz(N);
 #pragma unroll
-    for (int o = 32, n = 16; o >= 4; o >>= 1, n >>= 1) {
+    for (int st = 0; st < L; ++st) {
+        const int o = 32 >> st;
+        const int h = (N >> st) / 2;
         const bool upper = (lane & o) != 0;
 #pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-            const float give = upper ? r[i] : r[i + n / 2];
-            const float mine = upper ? r[i + n / 2] : r[i];
+        for (int i = 0; i < h; ++i) {
+            const float a = r[i], c = r[i + h];
+            const float give = upper ? a : c;
+            const float mine = upper ? c : a;
             r[i] = mine + __shfl_xor(give, o, kWave);
         }
     }
-    r[0] += __shfl_xor(r[0], 1, kWave);
-    r[0] += __shfl_xor(r[0], 2, kWave);
+#pragma unroll
+    for (int o = 1; o < (64 >> L); o <<= 1) r[0] += __shfl_xor(r[0], o, kWave);
 }
 
 // ---------------------------------------------------------------------------
@@ -77,7 +90,7 @@ __device__ __forceinline__ void reduce16_rows(float (&r)[16], int lane) {
 // (token, bank)
 // ---------------------------------------------------------------------------
 template <typename E>
-__global__ __launch_bounds__(256) void k_pred2_topk(const float* __restrict__ z,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_pred2_topk(const float* __restrict__ z,
                                                     const E* __restrict__ B,
                                                     const float* __restrict__ bias,
                                                     int rank, int d_i, int keep,
@@ -89,7 +102,7 @@ __global__ __launch_bounds__(256) void k_pred2_topk(const float* __restrict__ z,
     const int nb = d_i / kBank;
     const int64_t t = blockIdx.x / nb;
     const int b = (int)(blockIdx.x - t * nb);
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const float* zt = z + t * rank;
     const int nch = rank / 8;
     const int64_t row0 = (int64_t)b * kBank + 16 * wv;
@@ -98,12 +111,12 @@ __global__ __launch_bounds__(256) void k_pred2_topk(const float* __restrict__ z,
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     for (int c = lane; c < nch; c += 64) {
-        float zv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zv[e] = zt[8 * c + e];
         Raw<E> rb[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) rb[i].load(B + (row0 + i) * rank + 8 * c);
+        const float4 z0 = *reinterpret_cast<const float4*>(zt + 8 * c);
+        const float4 z1 = *reinterpret_cast<const float4*>(zt + 8 * c + 4);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float bv[8];
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(256) void k_pred2_topk(const float* __restrict__ z,
             for (int e = 0; e < 8; ++e) acc[i] = fmaf(zv[e], bv[e], acc[i]);
         }
     }
-    reduce16_rows(acc, lane);
+    reduce_rows<16>(acc, lane);
     if ((lane & 3) == 0) {
         const int r = lane >> 2;
         const float bj = bias ? bias[row0 + r] : 0.f;
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(256) void k_pred2_topk(const float* __restrict__ z,
 // ---------------------------------------------------------------------------
 // gate / up on kept rows: one wave per (token, kept channel)
 // ---------------------------------------------------------------------------
-template <typename E, int NC>
+template <typename E, int NC, bool EXACT>
 __global__ __launch_bounds__(256) void k_gateup(const E* __restrict__ x, const E* __restrict__ Wg,
                                                 const E* __restrict__ Wu,
                                                 const uint16_t* __restrict__ ids,
@@ -144,11 +157,12 @@ __global__ __launch_bounds__(256) void k_gateup(const E* __restrict__ x, const E
                                                 float* __restrict__ h, int d, int d_s,
                                                 int64_t n_work, int gate) {
     const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // wave-uniform work index: the id and logit below become scalar loads
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= n_work) return;
-    const int64_t t = w / d_s;
+    const unsigned t = (unsigned)w / (unsigned)d_s;
     const int64_t j = ids[w];
-    const E* xr = x + t * d;
+    const E* xr = x + (size_t)t * d;
     const E* gr = Wg + j * d;
     const E* ur = Wu + j * d;
     const int nch = d / 8;
@@ -158,12 +172,12 @@ __global__ __launch_bounds__(256) void k_gateup(const E* __restrict__ x, const E
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
             const int c = c0 + lane + 64 * k;
-            if (c < nch) { rg[k].load(gr + 8 * c); ru[k].load(ur + 8 * c); rx[k].load(xr + 8 * c); }
+            if (EXACT || c < nch) { rg[k].load(gr + 8 * c); ru[k].load(ur + 8 * c); rx[k].load(xr + 8 * c); }
         }
 #pragma unroll
         for (int k = 0; k < NC; ++k) {
             const int c = c0 + lane + 64 * k;
-            if (c < nch) {
+            if (EXACT || c < nch) {
                 float xv[8], gv[8], uv[8];
                 rx[k].decode(xv);
                 rg[k].decode(gv);
@@ -192,41 +206,58 @@ __global__ __launch_bounds__(256) void k_gateup(const E* __restrict__ x, const E
 constexpr int kGroup = 64;
 constexpr int kSlice = 512;
 
-template <typename E>
-__global__ __launch_bounds__(256) void k_down(const E* __restrict__ WdT,
+template <typename E, bool EXACT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_down(const E* __restrict__ WdT,
                                               const uint16_t* __restrict__ ids,
                                               const float* __restrict__ h,
                                               float* __restrict__ partial, int d, int d_s,
                                               int groups, int slices) {
     __shared__ float red[4][kSlice];
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t blk = blockIdx.x;
     const int s = (int)(blk % slices);
     const int64_t tg = blk / slices;
     const int g = (int)(tg % groups);
     const int64_t t = tg / groups;
     const int col = s * kSlice + lane * 8;
-    const bool active = col < d;
+    const bool active = EXACT || col < d;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     const int slot0 = g * kGroup + 16 * wv;
-    const int n_rows = min(16, d_s - slot0);
+    const int n_rows = EXACT ? 16 : min(16, d_s - slot0);
     if (active && n_rows > 0) {
         Raw<E> rw[16];
         float hv[16];
+        const size_t base = (size_t)t * d_s + slot0;
+        if constexpr (EXACT) {
+            // sixteen ids as two 16-byte words, made wave-uniform so that the
+            // row addresses live in scalar registers and all 16 row loads
+            // issue back to back
+            const uint4 i0 = *reinterpret_cast<const uint4*>(ids + base);
+            const uint4 i1 = *reinterpret_cast<const uint4*>(ids + base + 8);
+            const uint32_t iw[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i < n_rows) {
-                const int64_t slot = t * d_s + slot0 + i;
-                const int64_t j = ids[slot];
-                hv[i] = h[slot];
-                rw[i].load(WdT + j * d + col);
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t u = __builtin_amdgcn_readfirstlane(iw[k]);
+                rw[2 * k].load(WdT + (size_t)(u & 0xffffu) * d + col);
+                rw[2 * k + 1].load(WdT + (size_t)(u >> 16) * d + col);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hv[i] = h[base + i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i < n_rows) {
+                    const int64_t j = ids[base + i];
+                    hv[i] = h[base + i];
+                    rw[i].load(WdT + j * d + col);
+                }
             }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (i < n_rows) {
+            if (EXACT || i < n_rows) {
                 float wv8[8];
                 rw[i].decode(wv8);
 #pragma unroll
@@ -244,20 +275,185 @@ __global__ __launch_bounds__(256) void k_down(const E* __restrict__ WdT,
     }
 }
 
+// y = sum of the partials in a fixed order: workgroup = (token, 64 columns);
+// thread (column, quarter) sums every fourth group, then LDS joins quarters.
 template <typename E>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ partial, E* __restrict__ y,
-                                                int d, int groups, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int64_t t = i / d;
-    const int c = (int)(i - t * d);
-    const float* p = partial + t * groups * (int64_t)d + c;
+                                                int d, int groups, int col_blocks) {
+    __shared__ float red[4][64];
+    const int tid = threadIdx.x, cl = tid & 63, qr = tid >> 6;
+    const unsigned t = blockIdx.x / (unsigned)col_blocks;
+    const int c = (int)(blockIdx.x - t * col_blocks) * 64 + cl;
+    const bool active = c < d;
+    const float* p = partial + (size_t)t * groups * d + (active ? c : 0);
     float acc = 0.f;
-    for (int g = 0; g < groups; ++g) acc += p[(int64_t)g * d];
-    Elem<E>::store1(y + i, acc);
+    for (int g0 = qr; g0 < groups; g0 += 4 * 16) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int g = g0 + 4 * k;
+            v[k] = (active && g < groups) ? p[(size_t)g * d] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc += v[k];
+    }
+    red[qr][cl] = acc;
+    __syncthreads();
+    if (qr == 0 && active)
+        Elem<E>::store1(y + (size_t)t * d + c, (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]));
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode kernel for the method's layer width (d = 4096): one workgroup
+// of 8 waves per (token, bank) runs predictor layer 2 on the bank's 64 rows of
+// B, the bank top-k, gate/up on the KEEP kept rows and the bank's share of the
+// down projection over all d columns, written as one partial row of y.
+// The kept rows of W_d^T are requested right after the top-k so that they
+// stream in while gate/up is computed.
+// ---------------------------------------------------------------------------
+constexpr int kFusedD = 4096;
+
+template <int KEEP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
+                  const uint16_t* __restrict__ B, const float* __restrict__ bias,
+                  const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
+                  const uint16_t* __restrict__ WdT, int rank, int d_i, int gate,
+                  uint64_t* __restrict__ mask, float* __restrict__ logits,
+                  float* __restrict__ partial) {
+    constexpr int D = kFusedD, NW = 8, CPW = KEEP / NW, NCX = D / 8 / kWave;
+    static_assert(KEEP % NW == 0, "kept channels split evenly over the waves");
+    __shared__ uint4 xs[D / 8];
+    __shared__ float sp[kBank];
+    __shared__ int sid[KEEP];
+    __shared__ float spk[KEEP], sh[KEEP];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nb = d_i / kBank;
+    const unsigned t = blockIdx.x / (unsigned)nb;
+    const unsigned b = blockIdx.x - t * (unsigned)nb;
+    const int nch = rank / 8;
+
+    // predictor layer 2: wave wv takes rows 64 b + 8 wv .. + 8
+    const size_t row0 = (size_t)b * kBank + 8 * wv;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int c = lane; c < nch; c += kWave) {
+        Raw<uint16_t> rb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i].load(B + (row0 + i) * rank + 8 * c);
+        const float* zt = z + (size_t)t * rank + 8 * c;
+        const float4 z0 = *reinterpret_cast<const float4*>(zt);
+        const float4 z1 = *reinterpret_cast<const float4*>(zt + 4);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float bv[8];
+            rb[i].decode(bv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i] = fmaf(zv[e], bv[e], acc[i]);
+        }
+    }
+    xs[tid] = *reinterpret_cast<const uint4*>(x + (size_t)t * D + 8 * tid);
+    reduce_rows<8>(acc, lane);
+    if ((lane & 7) == 0) {
+        const int r = lane >> 3;
+        sp[8 * wv + r] = acc[0] + (bias ? bias[row0 + r] : 0.f);
+    }
+    __syncthreads();
+
+    // bank top-k
+    if (wv == 0) {
+        const float p = sp[lane];
+        const uint64_t sel = wave_bank_topk(rank_key(p), KEEP);
+        const int j = (int)b * kBank + lane;
+        if (logits) logits[(size_t)t * d_i + j] = p;
+        if (lane == 0) mask[(size_t)t * nb + b] = sel;
+        if ((sel >> lane) & 1ull) {
+            const int slot = (int)lanes_below(sel);
+            sid[slot] = j;
+            spk[slot] = p;
+        }
+    }
+    __syncthreads();
+
+    // kept rows of W_d^T: thread tid owns columns 8 tid .. 8 tid + 7
+    Raw<uint16_t> rd[KEEP];
+#pragma unroll
+    for (int k = 0; k < KEEP; ++k) {
+        const int j = __builtin_amdgcn_readfirstlane(sid[k]);
+        rd[k].load(WdT + (size_t)j * D + 8 * tid);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of gate/up
+
+    // gate / up: wave wv takes kept slots wv, wv + NW, ...
+    Raw<uint16_t> rg[CPW][NCX], ru[CPW][NCX];
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+        const int j = __builtin_amdgcn_readfirstlane(sid[wv + NW * k]);
+        const uint16_t* gr = Wg + (size_t)j * D;
+        const uint16_t* ur = Wu + (size_t)j * D;
+#pragma unroll
+        for (int m = 0; m < NCX; ++m) {
+            rg[k][m].load(gr + 8 * (lane + kWave * m));
+            ru[k][m].load(ur + 8 * (lane + kWave * m));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float u[CPW], v[CPW];
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) u[k] = v[k] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NCX; ++m) {
+        const uint4 xw = xs[lane + kWave * m];
+        const float xv[8] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y),
+                             bf16_lo(xw.z), bf16_hi(xw.z), bf16_lo(xw.w), bf16_hi(xw.w)};
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            float gv[8], uv[8];
+            rg[k][m].decode(gv);
+            ru[k][m].decode(uv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u[k] = fmaf(xv[e], gv[e], u[k]);
+                v[k] = fmaf(xv[e], uv[e], v[k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+        const float uu = wave_sum(u[k]), vv = wave_sum(v[k]);
+        if (lane == 0) {
+            const int slot = wv + NW * k;
+            const float sg = gate ? sigmoidf_dev(uu) : sigmoidf_dev(spk[slot]);
+            sh[slot] = sg * uu * vv;
+        }
+    }
+    __syncthreads();
+
+    // this bank's share of y over all columns
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KEEP; ++k) {
+        const float hk = sh[k];
+        float w8[8];
+        rd[k].decode(w8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(hk, w8[e], o[e]);
+    }
+    float* out = partial + ((size_t)t * nb + b) * D + 8 * tid;
+    reinterpret_cast<float4*>(out)[0] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<float4*>(out)[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
 int gather_groups(int d_s) { return (d_s + kGroup - 1) / kGroup; }
+
+bool fused_ok(const GatherArgs& a) {
+    return a.dt == Dt::BF16 && a.d == kFusedD && a.keep == 16 && a.rank % 8 == 0 && a.rank <= 512;
+}
 
 template <typename E, int NC>
 static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
@@ -265,30 +461,57 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
     const int nb = a.d_i / kBank;
     const int d_s = nb * a.keep;
     const int64_t T = a.T;
-    {
-        const int64_t n = T * a.rank;
-        xlaunch(a.events, 0, k_pred1<E, NC>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, x,
-                           static_cast<const E*>(a.A), a.z, a.d, a.rank, n,
-                           a.dt == Dt::BF16 ? 1 : 0);
+    const int nch = a.d / 8;
+    const int rb = a.dt == Dt::BF16 ? 1 : 0;
+    if (nch % (256 * 2) == 0)
+        xlaunch(a.events, 0, k_pred1<E, 2, true>, dim3((unsigned)(T * a.rank)), dim3(256), 0, s, x,
+                static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
+    else
+        xlaunch(a.events, 0, k_pred1<E, 2, false>, dim3((unsigned)(T * a.rank)), dim3(256), 0, s, x,
+                static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
+    if constexpr (sizeof(E) == 2) {
+        if (fused_ok(a)) {
+            xlaunch(a.events, 1, k_bank_fused<16>, dim3((unsigned)(T * nb)), dim3(512), 0, s, x, a.z,
+                    static_cast<const E*>(a.B), a.bias, static_cast<const E*>(a.W_g),
+                    static_cast<const E*>(a.W_u), static_cast<const E*>(a.W_dT), a.rank, a.d_i,
+                    a.gate, a.mask, a.logits, a.partial);
+            const int col_blocks = (a.d + 63) / 64;
+            xlaunch(a.events, 2, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
+                    a.partial, static_cast<E*>(a.y), a.d, nb, col_blocks);
+            skip_stages(a.events, 3, s);
+            return hipGetLastError();
+        }
     }
     xlaunch(a.events, 1, k_pred2_topk<E>, dim3((unsigned)(T * nb)), dim3(256), 0, s, a.z,
-                       static_cast<const E*>(a.B), a.bias, a.rank, a.d_i, a.keep, a.mask,
-                       a.logits, a.ids, a.pk);
+            static_cast<const E*>(a.B), a.bias, a.rank, a.d_i, a.keep, a.mask, a.logits, a.ids,
+            a.pk);
     {
         const int64_t n = T * d_s;
-        xlaunch(a.events, 2, k_gateup<E, NC>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, x,
-                           static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), a.ids,
-                           a.pk, a.h, a.d, d_s, n, a.gate);
+        const dim3 grid((unsigned)((n + 3) / 4));
+        if (nch % (64 * NC) == 0)
+            xlaunch(a.events, 2, k_gateup<E, NC, true>, grid, dim3(256), 0, s, x,
+                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), a.ids, a.pk, a.h,
+                    a.d, d_s, n, a.gate);
+        else
+            xlaunch(a.events, 2, k_gateup<E, NC, false>, grid, dim3(256), 0, s, x,
+                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), a.ids, a.pk, a.h,
+                    a.d, d_s, n, a.gate);
     }
     const int groups = gather_groups(d_s);
     const int slices = (a.d + kSlice - 1) / kSlice;
-    xlaunch(a.events, 3, k_down<E>, dim3((unsigned)(T * groups * slices)), dim3(256), 0, s,
-                       static_cast<const E*>(a.W_dT), a.ids, a.h, a.partial, a.d, d_s, groups,
-                       slices);
     {
-        const int64_t n = T * a.d;
-        xlaunch(a.events, 4, k_reduce<E>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                           a.partial, static_cast<E*>(a.y), a.d, groups, n);
+        const dim3 grid((unsigned)(T * groups * slices));
+        if (a.d % kSlice == 0 && d_s % kGroup == 0)
+            xlaunch(a.events, 3, k_down<E, true>, grid, dim3(256), 0, s,
+                    static_cast<const E*>(a.W_dT), a.ids, a.h, a.partial, a.d, d_s, groups, slices);
+        else
+            xlaunch(a.events, 3, k_down<E, false>, grid, dim3(256), 0, s,
+                    static_cast<const E*>(a.W_dT), a.ids, a.h, a.partial, a.d, d_s, groups, slices);
+    }
+    {
+        const int col_blocks = (a.d + 63) / 64;
+        xlaunch(a.events, 4, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
+                a.partial, static_cast<E*>(a.y), a.d, groups, col_blocks);
     }
     return hipGetLastError();
 }

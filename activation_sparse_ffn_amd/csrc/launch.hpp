@@ -16,6 +16,14 @@ constexpr int kStages = 5;
 // Launches one stage's kernel. With profiling events attached, events[2i]
 // and events[2i+1] take the start and end timestamps of this kernel's own
 // dispatch (hipExtLaunchKernel), so host launch gaps are not counted.
+// Records the start and stop events of stages [from, kStages) back to back,
+// for a path with fewer kernels than kStages.
+inline void skip_stages(void* const* events, int from, hipStream_t s) {
+    if (!events) return;
+    for (int i = 2 * from; i < 2 * kStages; ++i)
+        (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+}
+
 template <typename F, typename... Args>
 inline void xlaunch(void* const* events, int stage, F kernel, dim3 grid, dim3 block,
                     uint32_t shmem, hipStream_t s, Args... args) {
@@ -52,6 +60,7 @@ struct GatherArgs {
     void* const* events;            // null or 2 * kStages hipEvent_t
 };
 int gather_groups(int d_s);
+bool fused_ok(const GatherArgs& a);   // the fused per-bank decode kernel applies
 hipError_t launch_gather_forward(const GatherArgs& a, hipStream_t s);
 
 // ---- dense-masked MFMA path (bf16, many tokens) ---------------------------

@@ -14,6 +14,9 @@ resident in HBM:
            the 256 MB Infinity Cache. This is the default and the headline.
   batched  32 tokens per step, predictor output bias b ~ N(0, 0.5).
   prefill  4096 tokens per step with 1% outlier feature columns.
+  copy     not the layer: a plain 1 GiB device-to-device copy, timed and
+           used to scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of
+           a profiler run against a kernel of known traffic.
 
 The timed region replays a HIP graph of the steps (launch overhead removed).
 A second pass of the same steps launches each kernel with start/stop events
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["copy"], default="decode")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's bounded CPU sample")
@@ -74,7 +77,8 @@ def algorithmic(wl_name, shape, T, masks_union_frac=None):
     if wl_name == "decode":
         gateup = 2 * ds * row * T
         down = ds * row * T
-        return dict(pred=pred * T, gateup=gateup, down=down, bytes=pred * T + gateup + down,
+        return dict(pred=pred * T, pred_a=r * d * e * T, pred_b=d_i * r * e * T, gateup=gateup,
+                    down=down, bytes=pred * T + gateup + down,
                     flops=2 * T * (r * d + d_i * r + 3 * ds * d))
     # batched / prefill: weights of the union of the batch's kept channels
     u = masks_union_frac * d_i
@@ -110,6 +114,30 @@ def cpu_baseline(layer, T, budget_s):
                        f"{el:.1f} s wall, float64 numpy oracle")
 
 
+def copy_calibration(args):
+    """Attainable HBM bandwidth of a plain copy (read N + write N bytes)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k = max(args.steps // 64, 4)
+    e0.record()
+    for _ in range(k):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / k
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "device copy bandwidth (read + write)", "value": round(gbs, 1),
+                      "unit": "GB/s", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": k, "ms_per_copy": round(ms, 4), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +155,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.workload == "copy":
+        copy_calibration(args)
+        return
     cfg = WORKLOADS[args.workload]
     T = cfg["T"]
     n_layers = args.layers or cfg["layers"]
@@ -235,17 +266,22 @@ def main():
         f.set_stage_events(None)
     stage_us = stage_ms / n_prof * 1e3
     names = ffns[0].stage_names(T)
-    stages = {n: round(float(u), 3) for n, u in zip(names, stage_us)}
+    stages = {n: round(float(u), 3) for n, u in zip(names, stage_us) if n != "none"}
     log(f"stages (us): {stages}")
 
     # ---- roofline of the dominant kernel ------------------------------------
     if args.workload == "decode":
-        dom = "gateup"
+        if "bank_fused" in names:
+            dom, kname = "bank_fused", "k_bank_fused"
+            nbytes = alg["pred_b"] + alg["gateup"] + alg["down"]
+        else:
+            dom, kname = "gateup", "k_gateup"
+            nbytes = alg["gateup"]
         dur_s = stage_us[names.index(dom)] * 1e-6
-        achieved = alg["gateup"] / dur_s / 1e9
-        roof = dict(kernel="k_gateup", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+        achieved = nbytes / dur_s / 1e9
+        roof = dict(kernel=kname, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    bytes_per_launch=alg["gateup"], avg_us=round(float(stage_us[names.index(dom)]), 3))
+                    bytes_per_launch=nbytes, avg_us=round(float(stage_us[names.index(dom)]), 3))
     else:
         dom = "gateup_gemm"
         dur_s = stage_us[names.index(dom)] * 1e-6

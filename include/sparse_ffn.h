@@ -143,7 +143,8 @@ sffn_status_t sparse_ffn_set_stage_events(sffn_handle_t h, void* const* events,
                                           int32_t n_events);
 
 /* Name of stage i (0 <= i < SFFN_STAGES) of a forward of T tokens, e.g.
- * "gateup"; NULL when out of range. */
+ * "gateup"; "none" for a stage the chosen path does not have (its two events
+ * are recorded back to back); NULL when out of range. */
 const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i);
 
 /* Free the handle (host memory only; `packed` stays the caller's). */
