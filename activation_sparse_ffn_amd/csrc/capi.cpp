@@ -3,9 +3,12 @@
 //
 //   token-gather path  fp32 layers, and bf16 batches of at most
 //                      kGatherMaxTokens tokens: only kept rows are read
-//   MFMA path          bf16 batches above that: dense-masked contraction on
-//                      the matrix cores (the union of many tokens' masks is
-//                      nearly every channel)
+//   skinny MFMA path   bf16 batches of up to kSkinnyMaxTokens tokens: the
+//                      weights stream once through register-fed MFMA with
+//                      split K (the union of the batch's masks is nearly
+//                      every channel)
+//   MFMA path          larger bf16 batches: tiled dense-masked contraction on
+//                      the matrix cores
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -21,6 +24,7 @@
 namespace {
 
 constexpr int64_t kGatherMaxTokens = 4;
+constexpr int64_t kSkinnyMaxTokens = 64;
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
@@ -90,8 +94,12 @@ struct WsGather {
     size_t z, ids, pk, h, partial, mask, logits, total;
 };
 struct WsMfma {
-    size_t z, logits, mask, h, total;
+    size_t z, logits, mask, h, partial, gate, total;
 };
+
+bool use_skinny(const sffn_config_t& c, int64_t T) {
+    return !use_gather(c, T) && T <= kSkinnyMaxTokens && c.rank % 64 == 0;
+}
 
 WsGather ws_gather(const sffn_config_t& c, int64_t T) {
     const size_t nb = c.d_i / 64, ds = nb * c.keep;
@@ -119,6 +127,10 @@ WsMfma ws_mfma(const sffn_config_t& c, int64_t T) {
     w.logits = off; off += align_up((size_t)T * c.d_i * 4);
     w.mask = off;   off += align_up((size_t)T * nb * 8);
     w.h = off;      off += align_up((size_t)T * c.d_i * 2);
+    w.partial = off;
+    if (use_skinny(c, T)) off += align_up(sffn::skinny_partial_floats(T, c.d, c.rank, c.d_i) * 4);
+    w.gate = off;
+    if (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0) off += align_up(sffn::gate_tiles_bytes(T, c.d_i));
     w.total = off;
     return w;
 }
@@ -265,8 +277,11 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.logits = logits_out ? logits_out : at<float>(workspace, w.logits);
         a.mask = mask_out ? mask_out : at<uint64_t>(workspace, w.mask);
         a.h = at<uint16_t>(workspace, w.h);
+        a.gate_tiles = (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0)
+                           ? at<uint16_t>(workspace, w.gate) : nullptr;
         a.events = h->profiling ? h->events : nullptr;
-        he = sffn::launch_mfma_forward(a, s);
+        he = use_skinny(c, T) ? sffn::launch_skinny_forward(a, at<float>(workspace, w.partial), s)
+                              : sffn::launch_mfma_forward(a, s);
     }
     return hip_status(he, "sparse_ffn_forward");
 }

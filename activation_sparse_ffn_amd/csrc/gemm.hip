@@ -34,6 +34,7 @@ struct GemmParams {
     const float* bias;   // [N] or null
     const float* P;      // gate/up: logits [M, N]
     const uint64_t* mask;// gate/up: [M, N/64]
+    const uint16_t* G;   // gate/up, 256-row tiles: fp16 gate tiles instead of P and mask
     int gate;            // 0 predictor, 1 silu
 };
 
@@ -159,6 +160,206 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 x 64 tiles for the large contractions (gate/up and down of a
+// prefill chunk). Four waves, each owning a 128 x 128 block of C as 4 x 4
+// accumulator tiles of v_mfma_f32_32x32x16_bf16. A K step moves a 256-row x
+// 128-byte slab of each operand: eight lanes per row (whole 128-byte lines),
+// into LDS with 16-byte chunks XOR-swizzled by row (chunk g of row r at slot
+// g ^ ((r >> 1) & 7), so that the 16 consecutive rows one fragment read
+// touches fall on distinct banks), double-buffered so the next slab's global
+// loads are in flight while the matrix cores work on the current one.
+// For the gate/up epilogue the 256 B-rows of a tile are, in blocks of 64,
+// [W_g n0.., W_u n0.., W_g n0+64.., W_u n0+64..], so every wave holds u and v
+// of the same 64 channels and 128 tokens.
+// ---------------------------------------------------------------------------
+constexpr int TM = 256, TN = 256, TK = 64;
+constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
+
+__device__ __forceinline__ int slab_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int slab_off(int r, int g) { return r * 128 + ((g ^ slab_swz(r)) << 4); }
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
+    constexpr bool GU = EPI == EPI_GATEUP;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SLAB];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+
+    // tile order: workgroups land on the 8 XCDs round-robin; give each XCD a
+    // contiguous run of tiles, M fastest, so the tiles sharing a B slab run
+    // side by side in one L2
+    const unsigned G = gridDim.x, g = blockIdx.x;
+    const unsigned per = G / 8;
+    const unsigned gx = (G % 8 == 0) ? (g % 8) * per + g / 8 : g;
+    const int mt = (int)(gx % (unsigned)m_tiles), nt = (int)(gx / (unsigned)m_tiles);
+    const int64_t m0 = (int64_t)mt * TM;
+    const int n0 = nt * (GU ? TN / 2 : TN);          // gate/up: 128 channels per tile
+
+    // per-thread fetch rows: chunk c = tid + 256 i -> row c / 8, slot c % 8
+    const int fs = tid & 7;
+    const uint16_t* asrc[8];
+    const uint16_t* bsrc[8];
+    bool aok[8], bok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        const int gch = fs ^ slab_swz(r);
+        const int64_t m = m0 + r;
+        aok[i] = m < p.M;
+        asrc[i] = p.A + (aok[i] ? m : 0) * p.K + 8 * gch;
+        int n;
+        const uint16_t* base;
+        if constexpr (GU) {
+            const int grp = r >> 6;                    // 0..3
+            n = n0 + (grp >> 1) * 64 + (r & 63);
+            base = (grp & 1) ? p.B1 : p.B0;
+        } else {
+            n = n0 + r;
+            base = p.B0;
+        }
+        bok[i] = n < p.N;
+        bsrc[i] = base + (size_t)(bok[i] ? n : 0) * p.K + 8 * gch;
+    }
+    uint4 ra[8], rb[8];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ra[i] = aok[i] ? *reinterpret_cast<const uint4*>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
+            rb[i] = bok[i] ? *reinterpret_cast<const uint4*>(bsrc[i] + k0) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto stash = [&](int buf) {
+        char* As = smem + buf * 2 * SLAB;
+        char* Bs = As + SLAB;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = (tid >> 3) + 32 * i;
+            *reinterpret_cast<uint4*>(As + r * 128 + fs * 16) = ra[i];
+            *reinterpret_cast<uint4*>(Bs + r * 128 + fs * 16) = rb[i];
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int kt_n = p.K / TK;
+    const int r32 = lane & 31, hk = lane >> 5;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    // fragments of sub-step s of the slab in buffer buf
+    auto frags = [&](int buf, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+        const char* As = smem + buf * 2 * SLAB;
+        const char* Bs = As + SLAB;
+        const int gch = 2 * s + hk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(As + slab_off(wm * 128 + i * 32 + r32, gch));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * 128 + j * 32 + r32, gch));
+    };
+    auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    for (int kt = 0; kt < kt_n; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < kt_n;
+        if (more) fetch((kt + 1) * TK);
+        // the next sub-step's fragments load while the current one's 16 MFMAs run
+        bf16x8 a0[4], b0[4], a1[4], b1[4];
+        frags(buf, 0, a0, b0);
+        frags(buf, 1, a1, b1);
+        mma(a0, b0);
+        frags(buf, 2, a0, b0);
+        mma(a1, b1);
+        if (more) stash(buf ^ 1);          // the other buffer was released by the last barrier
+        frags(buf, 3, a1, b1);
+        mma(a0, b0);
+        mma(a1, b1);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5)
+    if constexpr (GU) {
+        if (p.G != nullptr) {
+            // the gate tile of this workgroup is one contiguous 256 x 128 block
+            const uint16_t* gt = p.G + ((size_t)mt * (p.N / kGateTileCols) + nt) * (TM * kGateTileCols);
+            const bool full = m0 + TM <= p.M;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint16_t gv[2][16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        gv[j][v] = (full || m0 + rt < p.M) ? gt[rt * kGateTileCols + wn * 64 + j * 32 + r32]
+                                                           : kGateDropped;
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+                    const int64_t m = m0 + rt;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = n0 + wn * 64 + j * 32 + r32;
+                        const float u = acc[i][j][v], vv = acc[i][j + 2][v];
+                        const bool keep = gv[j][v] != kGateDropped;
+                        const float sg = p.gate ? sigmoidf_dev(u)
+                                                : (float)__builtin_bit_cast(_Float16, gv[j][v]);
+                        if (full || m < p.M) p.Cb[m * p.N + n] = keep ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                    }
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < (GU ? 2 : 4); ++j) {
+            const int n = GU ? n0 + wn * 64 + j * 32 + r32 : n0 + wn * 128 + j * 32 + r32;
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t m = m0 + wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+                if (m >= p.M) continue;
+                const int64_t o = m * p.N + n;
+                if constexpr (EPI == EPI_BF16) {
+                    p.Cb[o] = f32_to_bf16(acc[i][j][v]);
+                } else if constexpr (EPI == EPI_F32_BIAS) {
+                    p.Cf[o] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.f);
+                } else {
+                    const float u = acc[i][j][v];
+                    const float vv = acc[i][j + 2][v];
+                    const bool keep = (p.mask[m * (p.N / kBank) + (n >> 6)] >> (n & 63)) & 1ull;
+                    const float sg = p.gate ? sigmoidf_dev(u) : sigmoidf_dev(p.P[o]);
+                    p.Cb[o] = keep ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                }
+            }
+        }
+}
+
+template <int EPI>
+static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
+    const int m_tiles = (int)((p.M + TM - 1) / TM);
+    const int n_tiles = (p.N + (EPI == EPI_GATEUP ? TN / 2 : TN) - 1) / (EPI == EPI_GATEUP ? TN / 2 : TN);
+    xlaunch(events, stage, k_gemm256<EPI>, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s, p,
+            m_tiles, n_tiles);
+}
+
 template <int EPI>
 static void gemm(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
     const int64_t mt = (p.M + BM - 1) / BM;
@@ -167,6 +368,8 @@ static void gemm(const GemmParams& p, hipStream_t s, void* const* events, int st
 }
 
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
+    // the 256-wide tiles need K to be a multiple of 64 and enough rows to fill them
+    const bool big = a.T >= 256 && a.d % 64 == 0 && a.d_i % 64 == 0;
     GemmParams g{};
     // Z = bf16(X A^T)
     g.A = a.x; g.B0 = a.A; g.M = a.T; g.N = a.rank; g.K = a.d; g.Cb = a.z;
@@ -176,17 +379,21 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     g.A = a.z; g.B0 = a.B; g.M = a.T; g.N = a.d_i; g.K = a.rank; g.Cf = a.logits; g.bias = a.bias;
     gemm<EPI_F32_BIAS>(g, s, a.events, 1);
     // mask
-    hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2);
+    const bool tiles = big && a.gate_tiles != nullptr && a.d_i % kGateTileCols == 0;
+    hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2,
+                                    tiles ? a.gate_tiles : nullptr, a.gate);
     if (e != hipSuccess) return e;
     // H = select(m, s u v, 0)
     g = GemmParams{};
     g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;
-    g.P = a.logits; g.mask = a.mask; g.gate = a.gate;
-    gemm<EPI_GATEUP>(g, s, a.events, 3);
+    g.P = a.logits; g.mask = a.mask; g.gate = a.gate; g.G = tiles ? a.gate_tiles : nullptr;
+    if (big) gemm256<EPI_GATEUP>(g, s, a.events, 3);
+    else gemm<EPI_GATEUP>(g, s, a.events, 3);
     // Y = bf16(H W_d^T)
     g = GemmParams{};
     g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
-    gemm<EPI_BF16>(g, s, a.events, 4);
+    if (big) gemm256<EPI_BF16>(g, s, a.events, 4);
+    else gemm<EPI_BF16>(g, s, a.events, 4);
     return hipGetLastError();
 }
 

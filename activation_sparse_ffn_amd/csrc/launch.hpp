@@ -33,9 +33,16 @@ inline void xlaunch(void* const* events, int stage, F kernel, dim3 grid, dim3 bl
 }
 
 // ---- bank top-k (one wave per (token, bank)) ------------------------------
+// Optional gate output for the 256 x 128 gate/up GEMM tiles (d_i % 128 == 0):
+// fp16 bits, tile-contiguous, G[t / 256][j / 128][t % 256][j % 128] =
+// sigmoid(p) (predictor gate) or 1 (silu gate) for kept channels, -1 for
+// dropped ones. Rows t >= T of the last tile are not written.
+constexpr int kGateTileRows = 256, kGateTileCols = 128;
+constexpr uint16_t kGateDropped = 0xbc00;   // fp16 -1.0
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s,
-                            void* const* events = nullptr, int stage = 0);
+                            void* const* events = nullptr, int stage = 0,
+                            uint16_t* gate_tiles = nullptr, int gate_mode = 0);
 
 // ---- token-gather path (VALU; decode and fp32 layers) ---------------------
 struct GatherArgs {
@@ -79,9 +86,16 @@ struct MfmaArgs {
     float* logits;          // [T, d_i]
     uint64_t* mask;         // [T, d_i/64]
     uint16_t* h;            // [T, d_i]    workspace
+    uint16_t* gate_tiles;   // fp16 gate tiles (see launch_bank_topk) or null
     void* const* events;    // null or 2 * kStages hipEvent_t
 };
+// bytes of the gate tiles for T tokens
+size_t gate_tiles_bytes(int64_t T, int d_i);
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s);
+
+// ---- skinny MFMA path (bf16, 4 < T <= 64, rank % 64 == 0) -----------------
+size_t skinny_partial_floats(int64_t T, int d, int rank, int d_i);
+hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t s);
 
 // ---- packing ---------------------------------------------------------------
 hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int cols,

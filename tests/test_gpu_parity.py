@@ -154,6 +154,22 @@ def test_bank_topk_bit_exact(keep):
             np.testing.assert_array_equal(ids_np[t], np.flatnonzero(m[t]))
 
 
+@pytest.mark.parametrize("keep", [1, 16, 64])
+def test_bank_topk_many_banks_per_wave(keep):
+    """Above 65536 (token, bank) words each wave selects 8 banks; a ragged
+    tail (4099 x 16 words is not a multiple of 32) and ties included."""
+    import activation_sparse_ffn_amd as sffn
+    p = wl.make_tie_logits(T=4099, d_i=1024, seed=8)
+    p[::7] = np.random.default_rng(3).standard_normal((len(p[::7]), 1024)).astype(np.float32)
+    mask, ids = sffn.bank_topk(dev(p), keep=keep, return_ids=True)
+    torch.cuda.synchronize()
+    m = o.bank_topk_mask(p, 64, keep)
+    np.testing.assert_array_equal(words(mask), o.mask_to_words(m))
+    ids_np = ids.cpu().numpy().view(np.uint16).astype(np.int64)
+    want = np.nonzero(m)[1].reshape(len(p), -1)
+    np.testing.assert_array_equal(ids_np, want)
+
+
 def test_bank_topk_stress_full_size():
     """32768 x 14336 fp32 logits with 5% exact ties per bank: the oracle on a
     seeded sample of tokens, structural properties on every bank."""
@@ -223,12 +239,12 @@ def test_forward_batched_full(full_layer, ffn_full_bias):
     assert 0.5 < frac < 1.0      # partial overlap across tokens
 
 
-@pytest.mark.parametrize("T", [5, 130])
+@pytest.mark.parametrize("T", [5, 40, 64, 130, 300])
 def test_forward_mfma_ragged_full(full_layer, ffn_full, T):
     x = wl.make_tokens(wl.FULL, T, seed=300 + T)
     y, mask, logits = ffn_full(dev(x), return_mask=True, return_logits=True)
     torch.cuda.synchronize()
-    rows = None if T <= 8 else [0, 1, 63, 64, 127, 128, 129]
+    rows = None if T <= 8 else [r for r in (0, 1, 31, 32, 39, 63, 64, 127, 128, 129, 255, 256, 299) if r < T]
     check_forward(full_layer, x, y, mask, logits, tokens=rows, bias=False)
 
 
@@ -265,7 +281,7 @@ def test_forward_long_context_chunks(full_layer, ffn_full):
     assert torch.equal(y2.view(torch.int16), y[C // 2:C // 2 + C].view(torch.int16))
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 5, 64, 200])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 64, 200, 300])
 @pytest.mark.parametrize("gate", ["pred", "silu"])
 def test_forward_mid_shapes(mid_layer, T, gate):
     ffn = make_ffn(mid_layer, bias=True, gate=gate)
