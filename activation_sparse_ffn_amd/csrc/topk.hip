@@ -47,6 +47,128 @@ __global__ __launch_bounds__(256) void k_bank_topk(const float* __restrict__ log
     }
 }
 
+// Many banks: one bank per lane. A wave stages the logits of 64 consecutive
+// (token, bank) words (16 KB, read with whole-line loads) in wave-private LDS,
+// 16-byte chunks XOR-swizzled by bank so that each lane can read its own bank
+// without bank conflicts. Each lane sorts its 64 order-preserving keys with a
+// bitonic network held in registers (max/min pairs, no branches), takes the
+// keep-th largest key as the threshold, and rebuilds the mask in channel
+// order: keys above the threshold are kept, keys equal to it are kept lowest
+// channel first until `keep` are taken -- the same rule as wave_bank_topk.
+__global__ __launch_bounds__(256) void k_bank_topk_lanes(const float* __restrict__ logits,
+                                                         int64_t n_words, int keep,
+                                                         uint64_t* __restrict__ mask,
+                                                         uint16_t* __restrict__ ids, int nb,
+                                                         uint16_t* __restrict__ gate,
+                                                         int gate_mode) {
+    __shared__ __attribute__((aligned(16))) float stage[4][kWave * kBank];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t w0 = ((int64_t)blockIdx.x * 4 + wv) * kWave;      // first word of this wave
+    float* st = stage[wv];
+    char* stb = reinterpret_cast<char*>(st);
+
+    // coalesced fetch: instruction q, lane l -> word q * 4 + l / 16, chunk l % 16
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int L = q * 4 + (lane >> 4), c = lane & 15;
+        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (w0 + L < n_words) val = *reinterpret_cast<const float4*>(logits + (w0 + L) * kBank + 4 * c);
+        *reinterpret_cast<float4*>(stb + L * 256 + ((c ^ (L & 15)) << 4)) = val;
+    }
+    const int64_t gw = w0 + lane;                  // this lane's word
+    const bool live = gw < n_words;
+
+    uint32_t k[kBank];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const float4 val = *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4));
+        k[4 * c + 0] = rank_key(val.x);
+        k[4 * c + 1] = rank_key(val.y);
+        k[4 * c + 2] = rank_key(val.z);
+        k[4 * c + 3] = rank_key(val.w);
+    }
+    // bitonic sort, descending
+#pragma unroll
+    for (int sz = 2; sz <= kBank; sz <<= 1)
+#pragma unroll
+        for (int j = sz >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < kBank; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint32_t a = k[i], b = k[l];
+                    const bool desc = (i & sz) == 0;
+                    k[i] = desc ? max(a, b) : min(a, b);
+                    k[l] = desc ? min(a, b) : max(a, b);
+                }
+            }
+    uint32_t thr = k[0];
+#pragma unroll
+    for (int i = 1; i < kBank; ++i) thr = (i == keep - 1) ? k[i] : thr;
+
+    // mask in channel order
+    uint32_t key[kBank];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const float4 val = *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4));
+        key[4 * c + 0] = rank_key(val.x);
+        key[4 * c + 1] = rank_key(val.y);
+        key[4 * c + 2] = rank_key(val.z);
+        key[4 * c + 3] = rank_key(val.w);
+    }
+    int n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < kBank; ++i) n_gt += key[i] > thr;
+    const int need = keep - n_gt;
+    int taken = 0;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < kBank; ++i) {
+        const bool eq_take = key[i] == thr && taken < need;
+        taken += eq_take;
+        const uint32_t bit = (key[i] > thr || eq_take) ? 1u : 0u;
+        if (i < 32) lo |= bit << i; else hi |= bit << (i - 32);
+    }
+    const uint64_t sel = ((uint64_t)hi << 32) | lo;
+    if (!live) return;
+    mask[gw] = sel;
+    const unsigned t = (unsigned)gw / (unsigned)nb;
+    const unsigned b = (unsigned)gw - t * (unsigned)nb;
+    if (ids != nullptr) {
+        int slot = 0;
+#pragma unroll
+        for (int i = 0; i < kBank; ++i)
+            if ((sel >> i) & 1ull) ids[gw * keep + slot++] = (uint16_t)(b * kBank + i);
+    }
+    if (gate != nullptr) {
+        const unsigned col_tiles = (unsigned)nb * kBank / kGateTileCols;
+        const unsigned j0 = b * kBank;
+        uint16_t* gp = gate + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
+                                  (kGateTileRows * kGateTileCols) +
+                       (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float4 v0 = *reinterpret_cast<const float4*>(stb + lane * 256 + (((2 * c) ^ (lane & 15)) << 4));
+            const float4 v1 = *reinterpret_cast<const float4*>(stb + lane * 256 + (((2 * c + 1) ^ (lane & 15)) << 4));
+            const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t hw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint16_t h2[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int i = 8 * c + 2 * e + q;
+                    const float g = gate_mode ? 1.f : sigmoidf_dev(pv[2 * e + q]);
+                    h2[q] = ((sel >> i) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)g) : kGateDropped;
+                }
+                hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+            }
+            *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+    }
+}
+
 size_t gate_tiles_bytes(int64_t T, int d_i) {
     return (size_t)((T + kGateTileRows - 1) / kGateTileRows) * kGateTileRows * d_i * 2;
 }
@@ -57,9 +179,8 @@ hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
     const int nb = d_i / kBank;
     const int64_t n_words = T * nb;
     if (n_words >= 65536) {
-        constexpr int BPW = 8;
-        const int64_t blocks = (n_words + 4 * BPW - 1) / (4 * BPW);
-        xlaunch(events, stage, k_bank_topk<BPW>, dim3((unsigned)blocks), dim3(256), 0, s, logits,
+        const int64_t blocks = (n_words + 4 * kWave - 1) / (4 * kWave);
+        xlaunch(events, stage, k_bank_topk_lanes, dim3((unsigned)blocks), dim3(256), 0, s, logits,
                 n_words, keep, mask, ids, nb, gate_tiles, gate_mode);
     } else {
         const int64_t blocks = (n_words + 3) / 4;
