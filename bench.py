@@ -14,6 +14,8 @@ resident in HBM:
            the 256 MB Infinity Cache. This is the default and the headline.
   batched  32 tokens per step, predictor output bias b ~ N(0, 0.5).
   prefill  4096 tokens per step with 1% outlier feature columns.
+  topk     the bank top-k alone over 32768 x 14336 fp32 logits with 5% exact
+           ties per bank (mask output), as GB/s against HBM.
   copy     not the layer: a plain 1 GiB device-to-device copy, timed and
            used to scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of
            a profiler run against a kernel of known traffic.
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["copy"], default="decode")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["topk", "copy"], default="decode")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's bounded CPU sample")
@@ -87,6 +89,20 @@ def algorithmic(wl_name, shape, T, masks_union_frac=None):
     return dict(pred=pred, gateup=gateup, down=down, bytes=pred + gateup + down,
                 flops=2 * T * (r * d + d_i * r + 3 * ds * d),
                 executed_flops=2 * T * (r * d + d_i * r + 3 * d_i * d))
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` (scaled FETCH_SIZE + WRITE_SIZE) from the
+    committed rocprofv3 counter summary, or None when it is not listed."""
+    path = os.path.join(ROOT, "profiles", "decode_T1_hbm_counters.md")
+    try:
+        for line in open(path):
+            cells = [c.strip() for c in line.split("|")]
+            if len(cells) > 5 and cells[1] == f"`{kernel}`":
+                return int(cells[4].replace(",", "")) + int(cells[5].replace(",", ""))
+    except (OSError, ValueError):
+        pass
+    return None
 
 
 def cpu_baseline(layer, T, budget_s):
@@ -138,6 +154,40 @@ def copy_calibration(args):
           flush=True)
 
 
+def topk_stress(args):
+    """bank_topk alone on the stress logits: bytes read + mask bytes written."""
+    import numpy as np
+    import torch
+    import activation_sparse_ffn_amd as sffn
+    import workloads as wl
+    cfg = wl.CONFIGS["topk_stress"]
+    t0 = time.time()
+    p = torch.from_numpy(wl.make_stress_logits(cfg["T"], cfg["d_i"], seed=0, tie_frac=cfg["tie_frac"])).cuda()
+    T, d_i = p.shape
+    mask = torch.empty((T, d_i // 64), dtype=torch.int64, device="cuda")
+    log(f"setup {time.time() - t0:.1f}s")
+    for _ in range(args.warmup):
+        sffn.bank_topk(p, 16, mask_out=mask)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        sffn.bank_topk(p, 16, mask_out=mask)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = p.numel() * 4 + mask.numel() * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    w = mask.cpu().numpy().view(np.uint64)
+    assert (np.bitwise_count(w) == 16).all()
+    print(json.dumps({"metric": "bank_topk stress: 32768 x 14336 fp32 logits, keep 16 of 64",
+                      "value": round(gbs, 1), "unit": "GB/s", "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms, 4), "banks_per_s": round(T * d_i / 64 / (ms * 1e-3), 1),
+                      "bytes_per_step": nbytes,
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -157,6 +207,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "copy":
         copy_calibration(args)
+        return
+    if args.workload == "topk":
+        topk_stress(args)
         return
     cfg = WORKLOADS[args.workload]
     T = cfg["T"]
@@ -280,7 +333,7 @@ def main():
         dur_s = stage_us[names.index(dom)] * 1e-6
         achieved = nbytes / dur_s / 1e9
         roof = dict(kernel=kname, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=profiled_traffic(kname),
                     bytes_per_launch=nbytes, avg_us=round(float(stage_us[names.index(dom)]), 3))
     else:
         dom = "gateup_gemm"
