@@ -275,32 +275,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
     }
 }
 
-// y = sum of the partials in a fixed order: workgroup = (token, 64 columns);
-// thread (column, quarter) sums every fourth group, then LDS joins quarters.
+// y = sum of the partial rows in a fixed order: workgroup = (token, 32
+// columns); thread (column, eighth) sums every eighth partial row with all of
+// its loads in flight, then LDS joins the eighths in order.
 template <typename E>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ partial, E* __restrict__ y,
                                                 int d, int groups, int col_blocks) {
-    __shared__ float red[4][64];
-    const int tid = threadIdx.x, cl = tid & 63, qr = tid >> 6;
+    constexpr int Q = 8, PER = 32;                 // eighths, loads per thread per pass
+    __shared__ float red[Q][32];
+    const int tid = threadIdx.x, cl = tid & 31, q = tid >> 5;
     const unsigned t = blockIdx.x / (unsigned)col_blocks;
-    const int c = (int)(blockIdx.x - t * col_blocks) * 64 + cl;
+    const int c = (int)(blockIdx.x - t * col_blocks) * 32 + cl;
     const bool active = c < d;
     const float* p = partial + (size_t)t * groups * d + (active ? c : 0);
     float acc = 0.f;
-    for (int g0 = qr; g0 < groups; g0 += 4 * 16) {
-        float v[16];
+    for (int g0 = q; g0 < groups; g0 += Q * PER) {
+        float v[PER];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int g = g0 + 4 * k;
+        for (int k = 0; k < PER; ++k) {
+            const int g = g0 + Q * k;
             v[k] = (active && g < groups) ? p[(size_t)g * d] : 0.f;
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) acc += v[k];
+        for (int k = 0; k < PER; ++k) acc += v[k];
     }
-    red[qr][cl] = acc;
+    red[q][cl] = acc;
     __syncthreads();
-    if (qr == 0 && active)
-        Elem<E>::store1(y + (size_t)t * d + c, (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]));
+    if (q == 0 && active) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < Q; ++k) s += red[k][cl];
+        Elem<E>::store1(y + (size_t)t * d + c, s);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -475,7 +481,7 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
                     static_cast<const E*>(a.B), a.bias, static_cast<const E*>(a.W_g),
                     static_cast<const E*>(a.W_u), static_cast<const E*>(a.W_dT), a.rank, a.d_i,
                     a.gate, a.mask, a.logits, a.partial);
-            const int col_blocks = (a.d + 63) / 64;
+            const int col_blocks = (a.d + 31) / 32;
             xlaunch(a.events, 2, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
                     a.partial, static_cast<E*>(a.y), a.d, nb, col_blocks);
             skip_stages(a.events, 3, s);
@@ -509,7 +515,7 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
                     static_cast<const E*>(a.W_dT), a.ids, a.h, a.partial, a.d, d_s, groups, slices);
     }
     {
-        const int col_blocks = (a.d + 63) / 64;
+        const int col_blocks = (a.d + 31) / 32;
         xlaunch(a.events, 4, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
                 a.partial, static_cast<E*>(a.y), a.d, groups, col_blocks);
     }

@@ -383,3 +383,38 @@ def test_stage_events_time_every_stage(mid_layer):
     assert all(0 < t < 100 for t in ts), ts
     assert ffn.stage_names(1)[2] == "gateup" and ffn.stage_names(64)[3] == "gateup_gemm"
     ffn.set_stage_events(None)
+
+
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_graph_capture_replays_match_eager(mid_layer, full_layer, ffn_full, T):
+    """Forwards captured in a HIP graph replay bit-identically to eager runs,
+    replay after replay, with other eager work and synchronisations between
+    the replays (no library call inside the graph may depend on state that
+    only the first replay sees)."""
+    ffn = ffn_full if T == 1 else make_ffn(mid_layer)
+    d = ffn.d
+    x = dev(wl.make_tokens(wl.FULL if T == 1 else MID, T, seed=500 + T))
+    other = dev(wl.make_tokens(wl.FULL if T == 1 else MID, T, seed=600 + T))
+    y_eager = ffn(x).clone()
+    m_eager = ffn(x, return_mask=True)[1].clone()
+    y = torch.empty_like(x)
+    mask = torch.empty((T, ffn.d_i // 64), dtype=torch.int64, device="cuda")
+    ws = torch.empty(ffn.workspace_size(T), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ffn(x, y=y, mask=mask, workspace=ws)          # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ffn(x, y=y, mask=mask, workspace=ws)
+    for r in range(4):
+        y.zero_()
+        mask.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), f"replay {r}"
+        assert torch.equal(mask, m_eager), f"replay {r}"
+        ffn(other, workspace=ws)                      # eager work reusing the workspace
+        torch.cuda.synchronize()
+    assert y.shape == (T, d)
