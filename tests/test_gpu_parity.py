@@ -161,6 +161,13 @@ def test_bank_topk_many_banks_per_wave(keep):
     import activation_sparse_ffn_amd as sffn
     p = wl.make_tie_logits(T=4099, d_i=1024, seed=8)
     p[::7] = np.random.default_rng(3).standard_normal((len(p[::7]), 1024)).astype(np.float32)
+    p[5, :64] = np.nan                        # a bank of NaNs only
+    p[6, :50] = np.nan                        # fewer than 64 - keep numbers
+    p[6, 64:128:5] = np.nan
+    p[7, ::3] = np.inf
+    p[8, 1::2] = -np.inf
+    p[9, :64] = np.where(np.arange(64) % 2, -0.0, 0.0)
+    p[10, 128:192] = np.float32(1e-45) * (np.arange(64) % 3 - 1)
     mask, ids = sffn.bank_topk(dev(p), keep=keep, return_ids=True)
     torch.cuda.synchronize()
     m = o.bank_topk_mask(p, 64, keep)
