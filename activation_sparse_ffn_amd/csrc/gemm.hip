@@ -179,13 +179,19 @@ constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab 
 __device__ __forceinline__ int slab_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int slab_off(int r, int g) { return r * 128 + ((g ^ slab_swz(r)) << 4); }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
+template <int EPI, int WN>
+__global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
+    // WN waves along N (2 or 4), 2 along M: each wave owns 128 x (256 / WN) of C
     constexpr bool GU = EPI == EPI_GATEUP;
+    constexpr int NT = 128 * WN;                     // threads
+    constexpr int WNC = TN / WN;                      // columns per wave
+    constexpr int NJ = WNC / 32;                      // accumulator tiles along N
+    constexpr int GB = WNC / 2;                       // gate/up interleave block (rows)
+    constexpr int NF = TM * 8 / NT;                   // 16-byte fetches per thread per operand
     __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SLAB];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
+    const int wm = wv / WN, wn = wv % WN;
 
     // tile order: workgroups land on the 8 XCDs round-robin; give each XCD a
     // contiguous run of tiles, M fastest, so the tiles sharing a B slab run
@@ -197,14 +203,15 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
     const int64_t m0 = (int64_t)mt * TM;
     const int n0 = nt * (GU ? TN / 2 : TN);          // gate/up: 128 channels per tile
 
-    // per-thread fetch rows: chunk c = tid + 256 i -> row c / 8, slot c % 8
+    // per-thread fetch rows: chunk c = tid + NT i -> row c / 8, slot c % 8.
+    // Gate/up B rows come in blocks of GB: [W_g, W_u] for channels n0 + GB b ..
     const int fs = tid & 7;
-    const uint16_t* asrc[8];
-    const uint16_t* bsrc[8];
-    bool aok[8], bok[8];
+    const uint16_t* asrc[NF];
+    const uint16_t* bsrc[NF];
+    bool aok[NF], bok[NF];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 3) + 32 * i;
+    for (int i = 0; i < NF; ++i) {
+        const int r = (tid >> 3) + (NT / 8) * i;
         const int gch = fs ^ slab_swz(r);
         const int64_t m = m0 + r;
         aok[i] = m < p.M;
@@ -212,9 +219,9 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
         int n;
         const uint16_t* base;
         if constexpr (GU) {
-            const int grp = r >> 6;                    // 0..3
-            n = n0 + (grp >> 1) * 64 + (r & 63);
-            base = (grp & 1) ? p.B1 : p.B0;
+            const int blk = r / GB;
+            n = n0 + (blk >> 1) * GB + (r % GB);
+            base = (blk & 1) ? p.B1 : p.B0;
         } else {
             n = n0 + r;
             base = p.B0;
@@ -222,10 +229,10 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
         bok[i] = n < p.N;
         bsrc[i] = base + (size_t)(bok[i] ? n : 0) * p.K + 8 * gch;
     }
-    uint4 ra[8], rb[8];
+    uint4 ra[NF], rb[NF];
     auto fetch = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NF; ++i) {
             ra[i] = aok[i] ? *reinterpret_cast<const uint4*>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
             rb[i] = bok[i] ? *reinterpret_cast<const uint4*>(bsrc[i] + k0) : make_uint4(0, 0, 0, 0);
         }
@@ -234,18 +241,18 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
         char* As = smem + buf * 2 * SLAB;
         char* Bs = As + SLAB;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = (tid >> 3) + 32 * i;
+        for (int i = 0; i < NF; ++i) {
+            const int r = (tid >> 3) + (NT / 8) * i;
             *reinterpret_cast<uint4*>(As + r * 128 + fs * 16) = ra[i];
             *reinterpret_cast<uint4*>(Bs + r * 128 + fs * 16) = rb[i];
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
     stash(0);
     __syncthreads();
     // fragments of sub-step s of the slab in buffer buf
-    auto frags = [&](int buf, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+    auto frags = [&](int buf, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
         const char* As = smem + buf * 2 * SLAB;
         const char* Bs = As + SLAB;
         const int gch = 2 * s + hk;
@@ -263,22 +270,22 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
         for (int i = 0; i < 4; ++i)
             af[i] = *reinterpret_cast<const bf16x8*>(As + slab_off(wm * 128 + i * 32 + r32, gch));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * 128 + j * 32 + r32, gch));
+        for (int j = 0; j < NJ; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * WNC + j * 32 + r32, gch));
     };
-    auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+    auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
     for (int kt = 0; kt < kt_n; ++kt) {
         const int buf = kt & 1;
         const bool more = kt + 1 < kt_n;
         if (more) fetch((kt + 1) * TK);
-        // the next sub-step's fragments load while the current one's 16 MFMAs run
-        bf16x8 a0[4], b0[4], a1[4], b1[4];
+        // the next sub-step's fragments load while the current one's MFMAs run
+        bf16x8 a0[4], b0[NJ], a1[4], b1[NJ];
         frags(buf, 0, a0, b0);
         frags(buf, 1, a1, b1);
         mma(a0, b0);
@@ -291,7 +298,9 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
         __syncthreads();
     }
 
-    // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5)
+    // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5);
+    // for gate/up, tile j < NJ / 2 holds u and tile j + NJ / 2 holds v of
+    // channels n0 + wn GB + 32 j + (lane & 31)
     if constexpr (GU) {
         if (p.G != nullptr) {
             // the gate tile of this workgroup is one contiguous 256 x 128 block
@@ -299,13 +308,13 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
             const bool full = m0 + TM <= p.M;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint16_t gv[2][16];
+                uint16_t gv[NJ / 2][16];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        gv[j][v] = (full || m0 + rt < p.M) ? gt[rt * kGateTileCols + wn * 64 + j * 32 + r32]
+                    for (int j = 0; j < NJ / 2; ++j)
+                        gv[j][v] = (full || m0 + rt < p.M) ? gt[rt * kGateTileCols + wn * GB + j * 32 + r32]
                                                            : kGateDropped;
                 }
 #pragma unroll
@@ -313,9 +322,9 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
                     const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
                     const int64_t m = m0 + rt;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int n = n0 + wn * 64 + j * 32 + r32;
-                        const float u = acc[i][j][v], vv = acc[i][j + 2][v];
+                    for (int j = 0; j < NJ / 2; ++j) {
+                        const int n = n0 + wn * GB + j * 32 + r32;
+                        const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
                         const bool keep = gv[j][v] != kGateDropped;
                         const float sg = p.gate ? sigmoidf_dev(u)
                                                 : (float)__builtin_bit_cast(_Float16, gv[j][v]);
@@ -329,8 +338,8 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < (GU ? 2 : 4); ++j) {
-            const int n = GU ? n0 + wn * 64 + j * 32 + r32 : n0 + wn * 128 + j * 32 + r32;
+        for (int j = 0; j < (GU ? NJ / 2 : NJ); ++j) {
+            const int n = GU ? n0 + wn * GB + j * 32 + r32 : n0 + wn * WNC + j * 32 + r32;
             if (n >= p.N) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
                     p.Cf[o] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.f);
                 } else {
                     const float u = acc[i][j][v];
-                    const float vv = acc[i][j + 2][v];
+                    const float vv = acc[i][j + NJ / 2][v];
                     const bool keep = (p.mask[m * (p.N / kBank) + (n >> 6)] >> (n & 63)) & 1ull;
                     const float sg = p.gate ? sigmoidf_dev(u) : sigmoidf_dev(p.P[o]);
                     p.Cb[o] = keep ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
@@ -352,12 +361,17 @@ __global__ __launch_bounds__(256) void k_gemm256(const GemmParams p, int m_tiles
         }
 }
 
+#ifndef SFFN_GEMM256_WN
+#define SFFN_GEMM256_WN 4        // waves along N in the 256 x 256 tiles (2: 4 waves, 4: 8 waves)
+#endif
+
 template <int EPI>
 static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
+    constexpr int WN = SFFN_GEMM256_WN;
     const int m_tiles = (int)((p.M + TM - 1) / TM);
     const int n_tiles = (p.N + (EPI == EPI_GATEUP ? TN / 2 : TN) - 1) / (EPI == EPI_GATEUP ? TN / 2 : TN);
-    xlaunch(events, stage, k_gemm256<EPI>, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s, p,
-            m_tiles, n_tiles);
+    xlaunch(events, stage, k_gemm256<EPI, WN>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0,
+            s, p, m_tiles, n_tiles);
 }
 
 template <int EPI>

@@ -152,6 +152,24 @@ def copy_calibration(args):
                       "unit": "GB/s", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                       "copies": k, "ms_per_copy": round(ms, 4), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}),
           flush=True)
+    del src, dst
+    # library bf16 GEMM of the down projection's shape (M = 4096 tokens,
+    # N = 4096, K = 14336): the attainable matrix-core rate for reference
+    a = torch.randn(4096, 14336, device="cuda").to(torch.bfloat16)
+    b = torch.randn(4096, 14336, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b.t())
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b.t())
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    tf = 2 * 4096 * 4096 * 14336 / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "library bf16 GEMM 4096 x 4096 x 14336 (torch.matmul)", "value": round(tf, 1),
+                      "unit": "TFLOP/s", "ms": round(ms, 4), "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4)}),
+          flush=True)
 
 
 def topk_stress(args):
