@@ -94,7 +94,7 @@ struct WsGather {
     size_t z, ids, pk, h, partial, mask, logits, total;
 };
 struct WsMfma {
-    size_t z, logits, mask, h, partial, gate, total;
+    size_t z, logits, mask, h, partial, gate, zpart, total;
 };
 
 bool use_skinny(const sffn_config_t& c, int64_t T) {
@@ -131,6 +131,9 @@ WsMfma ws_mfma(const sffn_config_t& c, int64_t T) {
     if (use_skinny(c, T)) off += align_up(sffn::skinny_partial_floats(T, c.d, c.rank, c.d_i) * 4);
     w.gate = off;
     if (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0) off += align_up(sffn::gate_tiles_bytes(T, c.d_i));
+    w.zpart = off;
+    const int zs = use_skinny(c, T) ? 1 : sffn::z_splits(T, c.d);
+    if (zs > 1) off += align_up((size_t)zs * T * c.rank * 4);
     w.total = off;
     return w;
 }
@@ -275,10 +278,13 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.y = static_cast<uint16_t*>(y);
         a.z = at<uint16_t>(workspace, w.z);
         a.logits = logits_out ? logits_out : at<float>(workspace, w.logits);
+        a.logits_requested = logits_out != nullptr;
         a.mask = mask_out ? mask_out : at<uint64_t>(workspace, w.mask);
         a.h = at<uint16_t>(workspace, w.h);
         a.gate_tiles = (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0)
                            ? at<uint16_t>(workspace, w.gate) : nullptr;
+        a.z_partial = (!use_skinny(c, T) && sffn::z_splits(T, c.d) > 1) ? at<float>(workspace, w.zpart)
+                                                                         : nullptr;
         a.events = h->profiling ? h->events : nullptr;
         he = use_skinny(c, T) ? sffn::launch_skinny_forward(a, at<float>(workspace, w.partial), s)
                               : sffn::launch_mfma_forward(a, s);
@@ -324,8 +330,13 @@ const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
     static const char* gather[] = {"pred1", "pred2_topk", "gateup", "down", "reduce"};
     static const char* fused[] = {"pred1", "bank_fused", "reduce", "none", "none"};
     static const char* mfma[] = {"pred1_gemm", "pred2_gemm", "bank_topk", "gateup_gemm", "down_gemm"};
+    static const char* mfma_fused[] = {"pred1_gemm", "pred2_topk_gemm", "none", "gateup_gemm", "down_gemm"};
     if (!h || i < 0 || i >= sffn::kStages) return nullptr;
-    if (!use_gather(h->cfg, T)) return mfma[i];
+    if (!use_gather(h->cfg, T)) {
+        const sffn_config_t& c = h->cfg;
+        const bool fused = !use_skinny(c, T) && sffn::mfma_fused_topk(T, c.d, c.d_i, c.rank);
+        return fused ? mfma_fused[i] : mfma[i];
+    }
     sffn::GatherArgs a{};
     a.dt = h->cfg.dtype == SFFN_BF16 ? sffn::Dt::BF16 : sffn::Dt::F32;
     a.d = h->cfg.d; a.d_i = h->cfg.d_i; a.rank = h->cfg.rank; a.keep = h->cfg.keep;

@@ -20,7 +20,7 @@
 
 namespace sffn {
 
-enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_GATEUP = 2 };
+enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_GATEUP = 2, EPI_PARTIAL = 3, EPI_TOPK = 4 };
 
 struct GemmParams {
     const uint16_t* A;   // [M, K]
@@ -36,16 +36,25 @@ struct GemmParams {
     const uint64_t* mask;// gate/up: [M, N/64]
     const uint16_t* G;   // gate/up, 256-row tiles: fp16 gate tiles instead of P and mask
     int gate;            // 0 predictor, 1 silu
+    int kn;              // EPI_PARTIAL: K range of one split (blockIdx.y selects the split)
+    // EPI_TOPK: logits (+ bias) go through LDS into the bank top-k; Cf receives
+    // the logits only when non-null
+    uint64_t* mask_w;    // [M, N/64]
+    uint16_t* gate_w;    // fp16 gate tiles
+    int keep;
 };
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LDS_STRIDE = BK + 8;   // elements; 80-byte rows keep 16-byte alignment
 
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_TOPK ? 2 : 1))) void k_gemm(const GemmParams p) {
     constexpr int NB = (EPI == EPI_GATEUP) ? 2 : 1;
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[NB][BN * LDS_STRIDE];
+    constexpr int STAGE_BYTES = (BM + NB * BN) * LDS_STRIDE * 2;
+    constexpr int TILE_BYTES = EPI == EPI_TOPK ? BM * BN * 4 : 0;     // fp32 logits tile
+    __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > TILE_BYTES ? STAGE_BYTES : TILE_BYTES];
+    uint16_t* const As = reinterpret_cast<uint16_t*>(smem);
+    auto BS = [&](int b) { return As + (BM + b * BN) * LDS_STRIDE; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -56,6 +65,8 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
     if (nt >= n_tiles) return;
     const int64_t m0 = mt * BM;
     const int n0 = nt * BN;
+    const int kn = EPI == EPI_PARTIAL ? p.kn : p.K;      // this workgroup's K range
+    const int kb = EPI == EPI_PARTIAL ? (int)blockIdx.y * p.kn : 0;
 
     // global -> register staging: each thread moves 2 chunks of 8 elements
     // per operand tile (128 rows x 4 chunks)
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
             *reinterpret_cast<uint4*>(&As[row * LDS_STRIDE + kc]) = ra[i];
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                *reinterpret_cast<uint4*>(&Bs[b][row * LDS_STRIDE + kc]) = rb[b][i];
+                *reinterpret_cast<uint4*>(&BS(b)[row * LDS_STRIDE + kc]) = rb[b][i];
         }
     };
 
@@ -98,12 +109,12 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
 
-    const int kt_n = p.K / BK;
-    load_tiles(0);
+    const int kt_n = kn / BK;
+    load_tiles(kb);
     for (int kt = 0; kt < kt_n; ++kt) {
         store_tiles();
         __syncthreads();
-        if (kt + 1 < kt_n) load_tiles((kt + 1) * BK);
+        if (kt + 1 < kt_n) load_tiles(kb + (kt + 1) * BK);
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
             const int ko = kk + 8 * (lane >> 5);
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int row = wn * 64 + j * 32 + (lane & 31);
-                    bfr[b][j] = *reinterpret_cast<const bf16x8*>(&Bs[b][row * LDS_STRIDE + ko]);
+                    bfr[b][j] = *reinterpret_cast<const bf16x8*>(&BS(b)[row * LDS_STRIDE + ko]);
                 }
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -134,6 +145,64 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
 
     // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5)
     const int nb64 = p.N / kBank;
+    if constexpr (EPI == EPI_TOPK) {
+        // logits (+ bias) into LDS as 256 bank-rows q = 2 row + (col >> 6) of
+        // 256 bytes, 16-byte chunks swizzled by q; the staging buffers are free
+        // (the K loop ended on a barrier)
+        char* tile = smem;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = wn * 64 + j * 32 + (lane & 31);
+                const int n = n0 + col;
+                const float bj = (p.bias && n < p.N) ? p.bias[n] : 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * 64 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * (lane >> 5);
+                    const int q = 2 * row + (col >> 6), c64 = col & 63;
+                    *reinterpret_cast<float*>(tile + q * 256 + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
+                        acc[0][i][j][v] + bj;
+                }
+            }
+        __syncthreads();
+        // one bank-row per lane
+        const int q = wv * kWave + lane;
+        const int row = q >> 1, bsel = q & 1;
+        const int64_t t = m0 + row;
+        const int j0 = n0 + bsel * kBank;
+        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(tile + q * 256 + ((c ^ (q & 15)) << 4)); };
+        const uint64_t sel = lane_select64(ld, p.keep);
+        if (t >= p.M || j0 >= p.N) return;
+        p.mask_w[t * nb64 + j0 / kBank] = sel;
+        if (p.Cf != nullptr) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) reinterpret_cast<float4*>(p.Cf + t * p.N + j0)[c] = ld(c);
+        }
+        const int col_tiles = p.N / kGateTileCols;
+        uint16_t* gp = p.gate_w + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
+                                      (kGateTileRows * kGateTileCols) +
+                       (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float4 v0 = ld(2 * c), v1 = ld(2 * c + 1);
+            const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t hw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint16_t h2[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int ch = 8 * c + 2 * e + k;
+                    const float gv = p.gate ? 1.f : sigmoidf_dev(pv[2 * e + k]);
+                    h2[k] = ((sel >> ch) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)gv) : kGateDropped;
+                }
+                hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+            }
+            *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -145,7 +214,9 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
                 const int64_t m = m0 + wm * 64 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * (lane >> 5);
                 if (m >= p.M) continue;
                 const int64_t o = m * p.N + n;
-                if constexpr (EPI == EPI_BF16) {
+                if constexpr (EPI == EPI_PARTIAL) {
+                    p.Cf[(int64_t)blockIdx.y * p.M * p.N + o] = acc[0][i][j][v];
+                } else if constexpr (EPI == EPI_BF16) {
                     p.Cb[o] = f32_to_bf16(acc[0][i][j][v]);
                 } else if constexpr (EPI == EPI_F32_BIAS) {
                     p.Cf[o] = acc[0][i][j][v] + (p.bias ? p.bias[n] : 0.f);
@@ -381,22 +452,68 @@ static void gemm(const GemmParams& p, hipStream_t s, void* const* events, int st
     xlaunch(events, stage, k_gemm<EPI>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, p);
 }
 
+// Sum of K-split partials in a fixed order, rounded to bf16.
+__global__ __launch_bounds__(256) void k_sum_splits_bf16(const float* __restrict__ partial,
+                                                         uint16_t* __restrict__ C, int splits,
+                                                         int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.f;
+    for (int k = 0; k < splits; ++k) acc += partial[(size_t)k * n + i];
+    C[i] = f32_to_bf16(acc);
+}
+
+bool mfma_fused_topk(int64_t T, int d, int d_i, int rank) {
+    return T >= 256 && d % 64 == 0 && d_i % kGateTileCols == 0 && rank % BK == 0;
+}
+
+int z_splits(int64_t T, int d) {
+    // split K of predictor layer 1 when the 128 x 128 tiles alone would leave
+    // most compute units idle
+    return (T >= 256 && d % (4 * BK) == 0) ? 4 : 1;
+}
+
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     // the 256-wide tiles need K to be a multiple of 64 and enough rows to fill them
     const bool big = a.T >= 256 && a.d % 64 == 0 && a.d_i % 64 == 0;
     GemmParams g{};
     // Z = bf16(X A^T)
     g.A = a.x; g.B0 = a.A; g.M = a.T; g.N = a.rank; g.K = a.d; g.Cb = a.z;
-    gemm<EPI_BF16>(g, s, a.events, 0);
+    const int zs = z_splits(a.T, a.d);
+    if (zs > 1 && a.z_partial != nullptr) {
+        g.Cf = a.z_partial; g.kn = a.d / zs;
+        const int64_t tiles = ((a.T + BM - 1) / BM) * ((a.rank + BN - 1) / BN);
+        hipEvent_t e0 = a.events ? static_cast<hipEvent_t>(a.events[0]) : nullptr;
+        hipEvent_t e1 = a.events ? static_cast<hipEvent_t>(a.events[1]) : nullptr;
+        hipExtLaunchKernelGGL(k_gemm<EPI_PARTIAL>, dim3((unsigned)tiles, (unsigned)zs), dim3(256), 0, s,
+                              e0, nullptr, 0u, g);
+        const int64_t n = a.T * (int64_t)a.rank;
+        hipExtLaunchKernelGGL(k_sum_splits_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                              nullptr, e1, 0u, (const float*)a.z_partial, a.z, zs, n);
+    } else {
+        gemm<EPI_BF16>(g, s, a.events, 0);
+    }
     // P = Z B^T + bias
     g = GemmParams{};
-    g.A = a.z; g.B0 = a.B; g.M = a.T; g.N = a.d_i; g.K = a.rank; g.Cf = a.logits; g.bias = a.bias;
-    gemm<EPI_F32_BIAS>(g, s, a.events, 1);
-    // mask
     const bool tiles = big && a.gate_tiles != nullptr && a.d_i % kGateTileCols == 0;
-    hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2,
-                                    tiles ? a.gate_tiles : nullptr, a.gate);
-    if (e != hipSuccess) return e;
+    if (tiles && mfma_fused_topk(a.T, a.d, a.d_i, a.rank)) {
+        // P, bank top-k and gate tiles in one kernel; the logits reach HBM
+        // only when the caller asked for them
+        g.A = a.z; g.B0 = a.B; g.M = a.T; g.N = a.d_i; g.K = a.rank; g.bias = a.bias;
+        g.Cf = a.logits_requested ? a.logits : nullptr;
+        g.mask_w = a.mask; g.gate_w = a.gate_tiles; g.keep = a.keep; g.gate = a.gate;
+        gemm<EPI_TOPK>(g, s, a.events, 1);
+        if (a.events) {
+            (void)hipEventRecord(static_cast<hipEvent_t>(a.events[4]), s);
+            (void)hipEventRecord(static_cast<hipEvent_t>(a.events[5]), s);
+        }
+    } else {
+        g.A = a.z; g.B0 = a.B; g.M = a.T; g.N = a.d_i; g.K = a.rank; g.Cf = a.logits; g.bias = a.bias;
+        gemm<EPI_F32_BIAS>(g, s, a.events, 1);
+        hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2,
+                                        tiles ? a.gate_tiles : nullptr, a.gate);
+        if (e != hipSuccess) return e;
+    }
     // H = select(m, s u v, 0)
     g = GemmParams{};
     g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;

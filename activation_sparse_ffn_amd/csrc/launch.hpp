@@ -87,8 +87,14 @@ struct MfmaArgs {
     uint64_t* mask;         // [T, d_i/64]
     uint16_t* h;            // [T, d_i]    workspace
     uint16_t* gate_tiles;   // fp16 gate tiles (see launch_bank_topk) or null
+    float* z_partial;       // [z_splits, T, rank] K-split partials of z, or null
+    bool logits_requested;  // logits points at the caller's logits_out
     void* const* events;    // null or 2 * kStages hipEvent_t
 };
+// K splits of predictor layer 1 on the MFMA path (1 = no split)
+int z_splits(int64_t T, int d);
+// predictor layer 2 and the bank top-k run as one kernel (with gate tiles)
+bool mfma_fused_topk(int64_t T, int d, int d_i, int rank);
 // bytes of the gate tiles for T tokens
 size_t gate_tiles_bytes(int64_t T, int d_i);
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s);

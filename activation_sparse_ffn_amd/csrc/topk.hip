@@ -47,56 +47,6 @@ __global__ __launch_bounds__(256) void k_bank_topk(const float* __restrict__ log
     }
 }
 
-// The 16th largest of 64 keys: sort four groups of 16 (descending bitonic
-// networks), merge them pairwise keeping the top 16 (max against the other
-// group reversed gives a bitonic sequence holding the top 16, which a
-// half-cleaner network sorts), and at the last level only the minimum of the
-// kept 16 is needed.
-__device__ __forceinline__ void sort16_desc(uint32_t* a) {
-#pragma unroll
-    for (int sz = 2; sz <= 16; sz <<= 1)
-#pragma unroll
-        for (int j = sz >> 1; j > 0; j >>= 1)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const uint32_t x = a[i], y = a[l];
-                    const bool desc = (i & sz) == 0;
-                    a[i] = desc ? max(x, y) : min(x, y);
-                    a[l] = desc ? min(x, y) : max(x, y);
-                }
-            }
-}
-// a, b sorted descending -> a holds the top 16 of both, sorted descending
-__device__ __forceinline__ void merge_top16(uint32_t* a, const uint32_t* b) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = max(a[i], b[15 - i]);
-#pragma unroll
-    for (int j = 8; j > 0; j >>= 1)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int l = i ^ j;
-            if (l > i) {
-                const uint32_t x = a[i], y = a[l];
-                a[i] = max(x, y);
-                a[l] = min(x, y);
-            }
-        }
-}
-__device__ __forceinline__ uint32_t kth16(uint32_t (&k)[kBank]) {
-    sort16_desc(k);
-    sort16_desc(k + 16);
-    sort16_desc(k + 32);
-    sort16_desc(k + 48);
-    merge_top16(k, k + 16);
-    merge_top16(k + 32, k + 48);
-    uint32_t t = max(k[0], k[47]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) t = min(t, max(k[i], k[47 - i]));
-    return t;
-}
-
 // Many banks: one bank per lane. A wave stages the logits of 64 consecutive
 // (token, bank) words (16 KB, read with whole-line loads) in wave-private LDS,
 // 16-byte chunks XOR-swizzled by bank so that each lane can read its own bank
@@ -129,69 +79,9 @@ __global__ __launch_bounds__(256) void k_bank_topk_lanes(const float* __restrict
     const int64_t gw = w0 + lane;                  // this lane's word
     const bool live = gw < n_words;
 
-    uint32_t k[kBank];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const float4 val = *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4));
-        k[4 * c + 0] = rank_key(val.x);
-        k[4 * c + 1] = rank_key(val.y);
-        k[4 * c + 2] = rank_key(val.z);
-        k[4 * c + 3] = rank_key(val.w);
-    }
-    uint32_t thr;
-    if (keep == 16) {
-        thr = kth16(k);
-    } else {
-        // bitonic sort, descending
-#pragma unroll
-        for (int sz = 2; sz <= kBank; sz <<= 1)
-#pragma unroll
-            for (int j = sz >> 1; j > 0; j >>= 1)
-#pragma unroll
-                for (int i = 0; i < kBank; ++i) {
-                    const int l = i ^ j;
-                    if (l > i) {
-                        const uint32_t a = k[i], b = k[l];
-                        const bool desc = (i & sz) == 0;
-                        k[i] = desc ? max(a, b) : min(a, b);
-                        k[l] = desc ? min(a, b) : max(a, b);
-                    }
-                }
-        thr = k[0];
-#pragma unroll
-        for (int i = 1; i < kBank; ++i) thr = (i == keep - 1) ? k[i] : thr;
-    }
-
-    // mask in channel order, comparing the logits against the threshold as
-    // floats: -0 == +0 and NaN fails every compare, as under the keys; a
-    // threshold key of 0 means the threshold lies among the NaNs
-    const bool nan_thr = thr == 0u;
-    const float thr_f = __uint_as_float((thr & 0x80000000u) ? (thr & 0x7fffffffu) : ~thr);
-    float fv[kBank];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const float4 val = *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4));
-        fv[4 * c + 0] = val.x;
-        fv[4 * c + 1] = val.y;
-        fv[4 * c + 2] = val.z;
-        fv[4 * c + 3] = val.w;
-    }
-    int n_gt = 0;
-#pragma unroll
-    for (int i = 0; i < kBank; ++i) n_gt += nan_thr ? !__builtin_isnan(fv[i]) : fv[i] > thr_f;
-    const int need = keep - n_gt;
-    int taken = 0;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < kBank; ++i) {
-        const bool gt = nan_thr ? !__builtin_isnan(fv[i]) : fv[i] > thr_f;
-        const bool eq = nan_thr ? __builtin_isnan(fv[i]) : fv[i] == thr_f;
-        const bool eq_take = eq && taken < need;
-        taken += eq_take;
-        const uint32_t bit = (gt || eq_take) ? 1u : 0u;
-        if (i < 32) lo |= bit << i; else hi |= bit << (i - 32);
-    }
-    const uint64_t sel = ((uint64_t)hi << 32) | lo;
+    const uint64_t sel = lane_select64(
+        [&](int c) { return *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4)); },
+        keep);
     if (!live) return;
     mask[gw] = sel;
     const unsigned t = (unsigned)gw / (unsigned)nb;

@@ -425,3 +425,19 @@ def test_graph_capture_replays_match_eager(mid_layer, full_layer, ffn_full, T):
         ffn(other, workspace=ws)                      # eager work reusing the workspace
         torch.cuda.synchronize()
     assert y.shape == (T, d)
+
+
+@pytest.mark.parametrize("T", [256, 300])
+def test_mask_and_output_do_not_depend_on_logits_request(full_layer, ffn_full_bias, T):
+    """With T >= 256 the bank top-k runs inside predictor layer 2 and the
+    logits reach memory only when asked for: the mask and y must be the
+    same either way, and the returned logits must give that mask."""
+    x = dev(wl.make_tokens(wl.FULL, T, seed=21))
+    y0, m0 = ffn_full_bias(x, return_mask=True)
+    y1, m1, p1 = ffn_full_bias(x, return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(words(m0), words(m1))
+    np.testing.assert_array_equal(host(y0), host(y1))
+    gl = host(p1)
+    np.testing.assert_array_equal(o.mask_to_words(o.bank_topk_mask(gl, 64, 16)), words(m1))
+    assert ffn_full_bias.stage_names(T)[1] == "pred2_topk_gemm"
