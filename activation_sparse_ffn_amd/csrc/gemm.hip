@@ -244,6 +244,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 // [W_g n0.., W_u n0.., W_g n0+64.., W_u n0+64..], so every wave holds u and v
 // of the same 64 channels and 128 tokens.
 // ---------------------------------------------------------------------------
+#ifndef SFFN_GEMM256_DMA
+#define SFFN_GEMM256_DMA 1       // slabs loaded global -> LDS directly (1) or through registers (0)
+#endif
+
 constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
 
@@ -259,7 +263,6 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     constexpr int NJ = WNC / 32;                      // accumulator tiles along N
     constexpr int GB = WNC / 2;                       // gate/up interleave block (rows)
     constexpr int NF = TM * 8 / NT;                   // 16-byte fetches per thread per operand
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SLAB];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WN, wn = wv % WN;
@@ -300,6 +303,98 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         bok[i] = n < p.N;
         bsrc[i] = base + (size_t)(bok[i] ? n : 0) * p.K + 8 * gch;
     }
+    f32x16 acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int kt_n = p.K / TK;
+    const int r32 = lane & 31, hk = lane >> 5;
+    // fragments of sub-step s of the slab pair at As (A slab, then B slab)
+    auto frags = [&](const char* As, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
+        const char* Bs = As + SLAB;
+        const int gch = 2 * s + hk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(As + slab_off(wm * 128 + i * 32 + r32, gch));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * WNC + j * 32 + r32, gch));
+    };
+    auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+#if SFFN_GEMM256_DMA
+    // Slabs go from global memory straight into LDS (global_load_lds_dwordx4:
+    // lane l of a wave writes the 16 bytes at base + 16 l, which is where the
+    // swizzled layout puts thread tid's chunk), so a fetch holds no registers
+    // and has a whole K step to land. Rows past M or N read row 0: their
+    // results are never stored. The two buffers are separate arrays and the
+    // loop is unrolled by two so that every LDS read names a buffer that no
+    // load in flight writes.
+    __shared__ __attribute__((aligned(16))) char buf0[2 * SLAB];
+    __shared__ __attribute__((aligned(16))) char buf1[2 * SLAB];
+    auto fetch = [&](int k0, char* dst) {
+        char* wbase = dst + wv * (kWave * 16);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(asrc[i] + k0),
+                (__attribute__((address_space(3))) void*)(wbase + i * NT * 16), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(bsrc[i] + k0),
+                (__attribute__((address_space(3))) void*)(wbase + SLAB + i * NT * 16), 16, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the MFMAs
+    };
+    auto landed = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);            // this wave's slab loads and LDS reads are done
+        __syncthreads();
+    };
+    // one MFMA group (a sub-step, 8 MFMAs) with the next group's fragment
+    // reads interleaved, one read per MFMA
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4 + NJ; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ - (4 + NJ), 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    bf16x8 xa[4], xb[NJ], ya[4], yb[NJ];
+    // K step kt from slab `cur` (sub-step 0 already in x); the barrier sits
+    // before the last sub-step, so that sub-step's MFMAs cover the barrier
+    // and the first reads of the next slab
+    auto step = [&](char* cur, const char* nxt, int kt) {
+        mma(xa, xb); frags(cur, 1, ya, yb); interleave();
+        mma(ya, yb); frags(cur, 2, xa, xb); interleave();
+        mma(xa, xb); frags(cur, 3, ya, yb); interleave();
+        landed();                                   // slab kt + 1 is in LDS, `cur` is free
+        if (kt + 2 < kt_n) fetch((kt + 2) * TK, cur);
+        mma(ya, yb);
+        frags(nxt, 0, xa, xb);       // after the last step: stale, unused (no load writes nxt then)
+        interleave();
+    };
+    fetch(0, buf0);
+    landed();
+    if (kt_n > 1) fetch(TK, buf1);
+    frags(buf0, 0, xa, xb);
+    int kt = 0;
+    for (; kt + 2 <= kt_n; kt += 2) {
+        step(buf0, buf1, kt);
+        step(buf1, buf0, kt + 1);
+    }
+    if (kt < kt_n) step(buf0, buf1, kt);       // odd count: the last slab is in buf0
+#else
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SLAB];
     uint4 ra[NF], rb[NF];
     auto fetch = [&](int k0) {
 #pragma unroll
@@ -318,56 +413,28 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
             *reinterpret_cast<uint4*>(Bs + r * 128 + fs * 16) = rb[i];
         }
     };
-
-    f32x16 acc[4][NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    const int kt_n = p.K / TK;
-    const int r32 = lane & 31, hk = lane >> 5;
     fetch(0);
     stash(0);
     __syncthreads();
-    // fragments of sub-step s of the slab in buffer buf
-    auto frags = [&](int buf, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
-        const char* As = smem + buf * 2 * SLAB;
-        const char* Bs = As + SLAB;
-        const int gch = 2 * s + hk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = *reinterpret_cast<const bf16x8*>(As + slab_off(wm * 128 + i * 32 + r32, gch));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * WNC + j * 32 + r32, gch));
-    };
-    auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    };
     for (int kt = 0; kt < kt_n; ++kt) {
         const int buf = kt & 1;
+        const char* As = smem + buf * 2 * SLAB;
         const bool more = kt + 1 < kt_n;
         if (more) fetch((kt + 1) * TK);
         // the next sub-step's fragments load while the current one's MFMAs run
         bf16x8 a0[4], b0[NJ], a1[4], b1[NJ];
-        frags(buf, 0, a0, b0);
-        frags(buf, 1, a1, b1);
+        frags(As, 0, a0, b0);
+        frags(As, 1, a1, b1);
         mma(a0, b0);
-        frags(buf, 2, a0, b0);
+        frags(As, 2, a0, b0);
         mma(a1, b1);
         if (more) stash(buf ^ 1);          // the other buffer was released by the last barrier
-        frags(buf, 3, a1, b1);
+        frags(As, 3, a1, b1);
         mma(a0, b0);
         mma(a1, b1);
         __syncthreads();
     }
+#endif
 
     // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5);
     // for gate/up, tile j < NJ / 2 holds u and tile j + NJ / 2 holds v of
