@@ -369,6 +369,21 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ - (4 + NJ), 0);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // gate/up with gate tiles: this workgroup's 256 x 128 fp16 gate tile is
+    // one contiguous 64 KB block; it is loaded during the last K step into
+    // the slab buffer that step frees, as a plain copy (row pitch 256 bytes)
+    const uint16_t* gtile = nullptr;
+    if constexpr (GU)
+        if (p.G != nullptr) gtile = p.G + ((size_t)mt * (p.N / kGateTileCols) + nt) * (TM * kGateTileCols);
+    auto fetch_gate = [&](char* dst) {
+        char* wbase = dst + wv * (kWave * 16);
+#pragma unroll
+        for (int i = 0; i < TM * kGateTileCols * 2 / (NT * 16); ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(gtile + (size_t)(tid + i * NT) * 8),
+                (__attribute__((address_space(3))) void*)(wbase + i * NT * 16), 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     bf16x8 xa[4], xb[NJ], ya[4], yb[NJ];
     // K step kt from slab `cur` (sub-step 0 already in x); the barrier sits
     // before the last sub-step, so that sub-step's MFMAs cover the barrier
@@ -379,6 +394,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         mma(xa, xb); frags(cur, 3, ya, yb); interleave();
         landed();                                   // slab kt + 1 is in LDS, `cur` is free
         if (kt + 2 < kt_n) fetch((kt + 2) * TK, cur);
+        else if (gtile != nullptr && kt + 1 == kt_n) fetch_gate(cur);
         mma(ya, yb);
         frags(nxt, 0, xa, xb);       // after the last step: stale, unused (no load writes nxt then)
         interleave();
@@ -393,6 +409,42 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         step(buf1, buf0, kt + 1);
     }
     if (kt < kt_n) step(buf0, buf1, kt);       // odd count: the last slab is in buf0
+    if constexpr (GU) {
+        if (gtile != nullptr) {
+            // H = select(kept, s u v, 0): gate values from the LDS copy of the
+            // gate tile; the bf16 tile is staged in the other buffer (16-byte
+            // chunks of rows 4..7 mod 8 swapped with chunks 4 apart, so the
+            // two half-waves write different banks) and leaves in 16-byte stores
+            landed();
+            const char* gbuf = (kt_n & 1) ? buf0 : buf1;     // `cur` of the last step
+            char* obuf = (kt_n & 1) ? buf1 : buf0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+#pragma unroll
+                    for (int j = 0; j < NJ / 2; ++j) {
+                        const int c = wn * GB + j * 32 + r32;
+                        const uint16_t g = *reinterpret_cast<const uint16_t*>(gbuf + rt * 256 + c * 2);
+                        const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
+                        const float sg = p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g);
+                        const uint16_t h = g != kGateDropped ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                        *reinterpret_cast<uint16_t*>(obuf + rt * 256 + ((c * 2) ^ (((rt >> 2) & 1) << 6))) = h;
+                    }
+                }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < TM * 16 / NT; ++i) {
+                const int ch = tid + i * NT, row = ch >> 4, c16 = ch & 15;
+                const int64_t m = m0 + row;
+                const uint4 val =
+                    *reinterpret_cast<const uint4*>(obuf + row * 256 + ((c16 ^ (((row >> 2) & 1) << 2)) << 4));
+                if (m < p.M) *reinterpret_cast<uint4*>(p.Cb + m * p.N + n0 + c16 * 8) = val;
+            }
+            return;
+        }
+    }
 #else
     __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SLAB];
     uint4 ra[NF], rb[NF];
