@@ -136,12 +136,12 @@ __device__ __forceinline__ uint64_t wave_bank_topk(uint32_t key, int keep) {
     return gt | __ballot(take);
 }
 
-// The 16th largest of 64 keys: sort four groups of 16 (descending bitonic
+// The 16th largest of 64 values: sort four groups of 16 (descending bitonic
 // networks), merge them pairwise keeping the top 16 (max against the other
 // group reversed gives a bitonic sequence holding the top 16, which a
 // half-cleaner network sorts), and at the last level only the minimum of the
-// kept 16 is needed.
-__device__ __forceinline__ void sort16_desc(uint32_t* a) {
+// kept 16 is needed. The values hold no NaN, so max/min are plain compares.
+__device__ __forceinline__ void sort16_desc(float* a) {
 #pragma unroll
     for (int sz = 2; sz <= 16; sz <<= 1)
 #pragma unroll
@@ -150,63 +150,77 @@ __device__ __forceinline__ void sort16_desc(uint32_t* a) {
             for (int i = 0; i < 16; ++i) {
                 const int l = i ^ j;
                 if (l > i) {
-                    const uint32_t x = a[i], y = a[l];
+                    const float x = a[i], y = a[l];
                     const bool desc = (i & sz) == 0;
-                    a[i] = desc ? max(x, y) : min(x, y);
-                    a[l] = desc ? min(x, y) : max(x, y);
+                    a[i] = desc ? fmaxf(x, y) : fminf(x, y);
+                    a[l] = desc ? fminf(x, y) : fmaxf(x, y);
                 }
             }
 }
 // a, b sorted descending -> a holds the top 16 of both, sorted descending
-__device__ __forceinline__ void merge_top16(uint32_t* a, const uint32_t* b) {
+__device__ __forceinline__ void merge_top16(float* a, const float* b) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = max(a[i], b[15 - i]);
+    for (int i = 0; i < 16; ++i) a[i] = fmaxf(a[i], b[15 - i]);
 #pragma unroll
     for (int j = 8; j > 0; j >>= 1)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int l = i ^ j;
             if (l > i) {
-                const uint32_t x = a[i], y = a[l];
-                a[i] = max(x, y);
-                a[l] = min(x, y);
+                const float x = a[i], y = a[l];
+                a[i] = fmaxf(x, y);
+                a[l] = fminf(x, y);
             }
         }
 }
-__device__ __forceinline__ uint32_t kth16(uint32_t (&k)[kBank]) {
+__device__ __forceinline__ float kth16(float (&k)[kBank]) {
     sort16_desc(k);
     sort16_desc(k + 16);
     sort16_desc(k + 32);
     sort16_desc(k + 48);
     merge_top16(k, k + 16);
     merge_top16(k + 32, k + 48);
-    uint32_t t = max(k[0], k[47]);
+    float t = fmaxf(k[0], k[47]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) t = min(t, max(k[i], k[47 - i]));
+    for (int i = 1; i < 16; ++i) t = fminf(t, fmaxf(k[i], k[47 - i]));
     return t;
 }
 
+// The n lowest set bits of x.
+__device__ __forceinline__ uint64_t lowest_bits(uint64_t x, int n) {
+    uint64_t r = 0;
+    for (int i = 0; i < n && x != 0; ++i) {
+        const uint64_t b = x & (~x + 1);
+        r |= b;
+        x ^= b;
+    }
+    return r;
+}
 
 // Keep mask of one 64-channel bank held entirely by one lane. `load(c)`
 // returns channels 4c .. 4c + 3 (c < 16) as a float4 and is called twice, so
-// the logits need not stay in registers across the sort. The keep-th largest
-// order-preserving key is found with sorting networks (branch-free max/min),
-// then the mask is rebuilt in channel order: logits above the threshold are
-// kept, logits equal to it lowest channel first until `keep` are taken -- the
-// same rule as wave_bank_topk. Float compares give -0 == +0 and put NaN below
-// every number; a threshold key of 0 means the threshold is among the NaNs.
+// the logits need not stay in registers across the selection.
+//
+// The keep-th largest value is found by sorting networks over the logits
+// with NaN mapped to -inf (fmaxf against -inf; -0 and +0 compare equal, as
+// under the ranking order). The mask is then every channel whose logit
+// compares >= that threshold. That set has exactly `keep` members unless
+// logits tie at the threshold -- then the channels above it are kept and the
+// tied ones lowest channel first -- or the threshold is -inf and NaNs are
+// needed to reach `keep`; NaNs rank below -inf and are taken last, lowest
+// channel first.
 template <typename Load>
 __device__ __forceinline__ uint64_t lane_select64(Load load, int keep) {
-    uint32_t k[kBank];
+    float k[kBank];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const float4 val = load(c);
-        k[4 * c + 0] = rank_key(val.x);
-        k[4 * c + 1] = rank_key(val.y);
-        k[4 * c + 2] = rank_key(val.z);
-        k[4 * c + 3] = rank_key(val.w);
+        k[4 * c + 0] = fmaxf(val.x, -__builtin_huge_valf());
+        k[4 * c + 1] = fmaxf(val.y, -__builtin_huge_valf());
+        k[4 * c + 2] = fmaxf(val.z, -__builtin_huge_valf());
+        k[4 * c + 3] = fmaxf(val.w, -__builtin_huge_valf());
     }
-    uint32_t thr;
+    float thr;
     if (keep == 16) {
         thr = kth16(k);
     } else {
@@ -219,18 +233,19 @@ __device__ __forceinline__ uint64_t lane_select64(Load load, int keep) {
                 for (int i = 0; i < kBank; ++i) {
                     const int l = i ^ j;
                     if (l > i) {
-                        const uint32_t a = k[i], b = k[l];
+                        const float a = k[i], b = k[l];
                         const bool desc = (i & sz) == 0;
-                        k[i] = desc ? max(a, b) : min(a, b);
-                        k[l] = desc ? min(a, b) : max(a, b);
+                        k[i] = desc ? fmaxf(a, b) : fminf(a, b);
+                        k[l] = desc ? fminf(a, b) : fmaxf(a, b);
                     }
                 }
         thr = k[0];
 #pragma unroll
         for (int i = 1; i < kBank; ++i) thr = (i == keep - 1) ? k[i] : thr;
     }
-    const bool nan_thr = thr == 0u;
-    const float thr_f = __uint_as_float((thr & 0x80000000u) ? (thr & 0x7fffffffu) : ~thr);
+    // reload the logits rather than keep all 64 live across the sort
+    // (a compiler-only memory barrier; no instruction)
+    __asm__ __volatile__("" ::: "memory");
     float fv[kBank];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -240,22 +255,34 @@ __device__ __forceinline__ uint64_t lane_select64(Load load, int keep) {
         fv[4 * c + 2] = val.z;
         fv[4 * c + 3] = val.w;
     }
-    int n_gt = 0;
-#pragma unroll
-    for (int i = 0; i < kBank; ++i) n_gt += nan_thr ? !__builtin_isnan(fv[i]) : fv[i] > thr_f;
-    const int need = keep - n_gt;
-    int taken = 0;
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < kBank; ++i) {
-        const bool gt = nan_thr ? !__builtin_isnan(fv[i]) : fv[i] > thr_f;
-        const bool eq = nan_thr ? __builtin_isnan(fv[i]) : fv[i] == thr_f;
-        const bool eq_take = eq && taken < need;
-        taken += eq_take;
-        const uint32_t bit = (gt || eq_take) ? 1u : 0u;
-        if (i < 32) lo |= bit << i; else hi |= bit << (i - 32);
+    for (int i = 0; i < 32; ++i) {
+        lo |= (uint32_t)(fv[i] >= thr) << i;
+        hi |= (uint32_t)(fv[32 + i] >= thr) << i;
     }
-    return ((uint64_t)hi << 32) | lo;
+    uint64_t sel = ((uint64_t)hi << 32) | lo;
+    const int n_ge = __popcll(sel);
+    if (n_ge == keep) return sel;
+    if (n_ge > keep) {
+        // ties at the threshold: everything above it, then the tied channels
+        uint32_t glo = 0, ghi = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            glo |= (uint32_t)(fv[i] > thr) << i;
+            ghi |= (uint32_t)(fv[32 + i] > thr) << i;
+        }
+        const uint64_t gt = ((uint64_t)ghi << 32) | glo;
+        return gt | lowest_bits(sel & ~gt, keep - __popcll(gt));
+    }
+    // fewer than keep non-NaN logits: the NaNs fill up, lowest channel first
+    uint32_t nlo = 0, nhi = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        nlo |= (uint32_t)__builtin_isnan(fv[i]) << i;
+        nhi |= (uint32_t)__builtin_isnan(fv[32 + i]) << i;
+    }
+    return sel | lowest_bits(((uint64_t)nhi << 32) | nlo, keep - n_ge);
 }
 
 }  // namespace sffn

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_bank_topk_lanes(const float* __restrict
     const bool live = gw < n_words;
 
     const uint64_t sel = lane_select64(
-        [&](int c) { return *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4)); },
+        [stb, lane](int c) { return *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4)); },
         keep);
     if (!live) return;
     mask[gw] = sel;
