@@ -244,9 +244,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 // [W_g n0.., W_u n0.., W_g n0+64.., W_u n0+64..], so every wave holds u and v
 // of the same 64 channels and 128 tokens.
 // ---------------------------------------------------------------------------
-#ifndef SFFN_GEMM256_DMA
-#define SFFN_GEMM256_DMA 1       // slabs loaded global -> LDS directly (1) or through registers (0)
-#endif
 
 constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
@@ -263,56 +260,58 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     constexpr int NJ = WNC / 32;                      // accumulator tiles along N
     constexpr int GB = WNC / 2;                       // gate/up interleave block (rows)
     constexpr int NF = TM * 8 / NT;                   // 16-byte fetches per thread per operand
+    constexpr int TNC = GU ? TN / 2 : TN;             // output columns per tile
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WN, wn = wv % WN;
+    const int r32 = lane & 31, hk = lane >> 5;
+    const int kt_n = p.K / TK;
 
-    // tile order: workgroups land on the 8 XCDs round-robin; give each XCD a
-    // contiguous run of tiles, M fastest, so the tiles sharing a B slab run
-    // side by side in one L2
-    const unsigned G = gridDim.x, g = blockIdx.x;
-    const unsigned per = G / 8;
-    const unsigned gx = (G % 8 == 0) ? (g % 8) * per + g / 8 : g;
+    // Tile order: workgroups land on the 8 XCDs round-robin, so tile g runs on
+    // XCD g % 8; each XCD gets a contiguous run of tiles, M fastest, so the
+    // tiles sharing a B slab run side by side in one L2.
+    const unsigned total = gridDim.x, g = blockIdx.x;
+    const unsigned gx = (total % 8 == 0) ? (g % 8) * (total / 8) + g / 8 : g;
     const int mt = (int)(gx % (unsigned)m_tiles), nt = (int)(gx / (unsigned)m_tiles);
     const int64_t m0 = (int64_t)mt * TM;
-    const int n0 = nt * (GU ? TN / 2 : TN);          // gate/up: 128 channels per tile
+    const int n0 = nt * TNC;
 
     // per-thread fetch rows: chunk c = tid + NT i -> row c / 8, slot c % 8.
     // Gate/up B rows come in blocks of GB: [W_g, W_u] for channels n0 + GB b ..
+    // Rows past M or N read row 0: their results are never stored.
     const int fs = tid & 7;
     const uint16_t* asrc[NF];
     const uint16_t* bsrc[NF];
-    bool aok[NF], bok[NF];
+    auto sources = [&](int64_t mb, int nb0) {
 #pragma unroll
-    for (int i = 0; i < NF; ++i) {
-        const int r = (tid >> 3) + (NT / 8) * i;
-        const int gch = fs ^ slab_swz(r);
-        const int64_t m = m0 + r;
-        aok[i] = m < p.M;
-        asrc[i] = p.A + (aok[i] ? m : 0) * p.K + 8 * gch;
-        int n;
-        const uint16_t* base;
-        if constexpr (GU) {
-            const int blk = r / GB;
-            n = n0 + (blk >> 1) * GB + (r % GB);
-            base = (blk & 1) ? p.B1 : p.B0;
-        } else {
-            n = n0 + r;
-            base = p.B0;
+        for (int i = 0; i < NF; ++i) {
+            const int r = (tid >> 3) + (NT / 8) * i;
+            const int gch = fs ^ slab_swz(r);
+            const int64_t m = mb + r;
+            asrc[i] = p.A + (m < p.M ? m : 0) * p.K + 8 * gch;
+            int n;
+            const uint16_t* base;
+            if constexpr (GU) {
+                const int blk = r / GB;
+                n = nb0 + (blk >> 1) * GB + (r % GB);
+                base = (blk & 1) ? p.B1 : p.B0;
+            } else {
+                n = nb0 + r;
+                base = p.B0;
+            }
+            bsrc[i] = base + (size_t)(n < p.N ? n : 0) * p.K + 8 * gch;
         }
-        bok[i] = n < p.N;
-        bsrc[i] = base + (size_t)(bok[i] ? n : 0) * p.K + 8 * gch;
-    }
-    f32x16 acc[4][NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    };
+    // gate/up with gate tiles: the 256 x 128 fp16 gate tile of an output block
+    // is one contiguous 64 KB block
+    auto gate_tile = [&](int mtile, int ntile) -> const uint16_t* {
+        if constexpr (GU)
+            if (p.G != nullptr)
+                return p.G + ((size_t)mtile * (p.N / kGateTileCols) + ntile) * (TM * kGateTileCols);
+        return nullptr;
+    };
 
-    const int kt_n = p.K / TK;
-    const int r32 = lane & 31, hk = lane >> 5;
+    f32x16 acc[4][NJ];
     // fragments of sub-step s of the slab pair at As (A slab, then B slab)
     auto frags = [&](const char* As, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[NJ]) {
         const char* Bs = As + SLAB;
@@ -331,14 +330,12 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
             for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
-#if SFFN_GEMM256_DMA
     // Slabs go from global memory straight into LDS (global_load_lds_dwordx4:
     // lane l of a wave writes the 16 bytes at base + 16 l, which is where the
     // swizzled layout puts thread tid's chunk), so a fetch holds no registers
-    // and has a whole K step to land. Rows past M or N read row 0: their
-    // results are never stored. The two buffers are separate arrays and the
-    // loop is unrolled by two so that every LDS read names a buffer that no
-    // load in flight writes.
+    // and has a whole K step to land. The two buffers are separate arrays and
+    // the loop is unrolled by two so that every LDS read names a buffer that
+    // no load in flight writes.
     __shared__ __attribute__((aligned(16))) char buf0[2 * SLAB];
     __shared__ __attribute__((aligned(16))) char buf1[2 * SLAB];
     auto fetch = [&](int k0, char* dst) {
@@ -354,8 +351,18 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         }
         __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the MFMAs
     };
+    // the gate tile as a plain copy (row pitch 256 bytes)
+    auto fetch_gate = [&](const uint16_t* gt, char* dst) {
+        char* wbase = dst + wv * (kWave * 16);
+#pragma unroll
+        for (int i = 0; i < TM * kGateTileCols * 2 / (NT * 16); ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(gt + (size_t)(tid + i * NT) * 8),
+                (__attribute__((address_space(3))) void*)(wbase + i * NT * 16), 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto landed = [&]() {
-        __builtin_amdgcn_s_waitcnt(0);            // this wave's slab loads and LDS reads are done
+        __builtin_amdgcn_s_waitcnt(0);            // this wave's loads and LDS reads are done
         __syncthreads();
     };
     // one MFMA group (a sub-step, 8 MFMAs) with the next group's fragment
@@ -369,22 +376,8 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ - (4 + NJ), 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // gate/up with gate tiles: this workgroup's 256 x 128 fp16 gate tile is
-    // one contiguous 64 KB block; it is loaded during the last K step into
-    // the slab buffer that step frees, as a plain copy (row pitch 256 bytes)
-    const uint16_t* gtile = nullptr;
-    if constexpr (GU)
-        if (p.G != nullptr) gtile = p.G + ((size_t)mt * (p.N / kGateTileCols) + nt) * (TM * kGateTileCols);
-    auto fetch_gate = [&](char* dst) {
-        char* wbase = dst + wv * (kWave * 16);
-#pragma unroll
-        for (int i = 0; i < TM * kGateTileCols * 2 / (NT * 16); ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(gtile + (size_t)(tid + i * NT) * 8),
-                (__attribute__((address_space(3))) void*)(wbase + i * NT * 16), 16, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
     bf16x8 xa[4], xb[NJ], ya[4], yb[NJ];
+    const uint16_t* gtile = nullptr;          // gate tile of the current output block, if any
     // K step kt from slab `cur` (sub-step 0 already in x); the barrier sits
     // before the last sub-step, so that sub-step's MFMAs cover the barrier
     // and the first reads of the next slab
@@ -394,11 +387,20 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         mma(xa, xb); frags(cur, 3, ya, yb); interleave();
         landed();                                   // slab kt + 1 is in LDS, `cur` is free
         if (kt + 2 < kt_n) fetch((kt + 2) * TK, cur);
-        else if (gtile != nullptr && kt + 1 == kt_n) fetch_gate(cur);
+        else if (gtile != nullptr && kt + 1 == kt_n) fetch_gate(gtile, cur);
         mma(ya, yb);
         frags(nxt, 0, xa, xb);       // after the last step: stale, unused (no load writes nxt then)
         interleave();
     };
+
+    sources(m0, n0);
+    gtile = gate_tile(mt, nt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     fetch(0, buf0);
     landed();
     if (kt_n > 1) fetch(TK, buf1);
@@ -409,28 +411,36 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         step(buf1, buf0, kt + 1);
     }
     if (kt < kt_n) step(buf0, buf1, kt);       // odd count: the last slab is in buf0
+    char* gbuf = (kt_n & 1) ? buf0 : buf1;     // the last step's `cur`
+
+    // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2)
+    // + 4 (lane >> 5); for gate/up, tile j < NJ / 2 holds u and tile
+    // j + NJ / 2 holds v of channels n0 + wn GB + 32 j + (lane & 31)
     if constexpr (GU) {
         if (gtile != nullptr) {
-            // H = select(kept, s u v, 0): gate values from the LDS copy of the
-            // gate tile; the bf16 tile is staged in the other buffer (16-byte
-            // chunks of rows 4..7 mod 8 swapped with chunks 4 apart, so the
-            // two half-waves write different banks) and leaves in 16-byte stores
+            // H = select(kept, s u v, 0) with the gate values of the LDS
+            // copy of the gate tile, written over them in place (each
+            // element is read and written by one lane); the bf16 tile then
+            // leaves in 16-byte stores
             landed();
-            const char* gbuf = (kt_n & 1) ? buf0 : buf1;     // `cur` of the last step
-            char* obuf = (kt_n & 1) ? buf1 : buf0;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+                for (int j = 0; j < NJ / 2; ++j) {
+                    // 16 reads in flight, then the 16 writes
+                    uint16_t* e[16];
+                    uint16_t g[16];
 #pragma unroll
-                    for (int j = 0; j < NJ / 2; ++j) {
-                        const int c = wn * GB + j * 32 + r32;
-                        const uint16_t g = *reinterpret_cast<const uint16_t*>(gbuf + rt * 256 + c * 2);
+                    for (int v = 0; v < 16; ++v) {
+                        const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+                        e[v] = reinterpret_cast<uint16_t*>(gbuf + rt * 256) + wn * GB + j * 32 + r32;
+                        g[v] = *e[v];
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
                         const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
-                        const float sg = p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g);
-                        const uint16_t h = g != kGateDropped ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
-                        *reinterpret_cast<uint16_t*>(obuf + rt * 256 + ((c * 2) ^ (((rt >> 2) & 1) << 6))) = h;
+                        const float sg = p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g[v]);
+                        *e[v] = g[v] != kGateDropped ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
                     }
                 }
             __syncthreads();
@@ -438,89 +448,8 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
             for (int i = 0; i < TM * 16 / NT; ++i) {
                 const int ch = tid + i * NT, row = ch >> 4, c16 = ch & 15;
                 const int64_t m = m0 + row;
-                const uint4 val =
-                    *reinterpret_cast<const uint4*>(obuf + row * 256 + ((c16 ^ (((row >> 2) & 1) << 2)) << 4));
+                const uint4 val = *reinterpret_cast<const uint4*>(gbuf + row * 256 + c16 * 16);
                 if (m < p.M) *reinterpret_cast<uint4*>(p.Cb + m * p.N + n0 + c16 * 8) = val;
-            }
-            return;
-        }
-    }
-#else
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * SLAB];
-    uint4 ra[NF], rb[NF];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            ra[i] = aok[i] ? *reinterpret_cast<const uint4*>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
-            rb[i] = bok[i] ? *reinterpret_cast<const uint4*>(bsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto stash = [&](int buf) {
-        char* As = smem + buf * 2 * SLAB;
-        char* Bs = As + SLAB;
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            const int r = (tid >> 3) + (NT / 8) * i;
-            *reinterpret_cast<uint4*>(As + r * 128 + fs * 16) = ra[i];
-            *reinterpret_cast<uint4*>(Bs + r * 128 + fs * 16) = rb[i];
-        }
-    };
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int kt = 0; kt < kt_n; ++kt) {
-        const int buf = kt & 1;
-        const char* As = smem + buf * 2 * SLAB;
-        const bool more = kt + 1 < kt_n;
-        if (more) fetch((kt + 1) * TK);
-        // the next sub-step's fragments load while the current one's MFMAs run
-        bf16x8 a0[4], b0[NJ], a1[4], b1[NJ];
-        frags(As, 0, a0, b0);
-        frags(As, 1, a1, b1);
-        mma(a0, b0);
-        frags(As, 2, a0, b0);
-        mma(a1, b1);
-        if (more) stash(buf ^ 1);          // the other buffer was released by the last barrier
-        frags(As, 3, a1, b1);
-        mma(a0, b0);
-        mma(a1, b1);
-        __syncthreads();
-    }
-#endif
-
-    // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5);
-    // for gate/up, tile j < NJ / 2 holds u and tile j + NJ / 2 holds v of
-    // channels n0 + wn GB + 32 j + (lane & 31)
-    if constexpr (GU) {
-        if (p.G != nullptr) {
-            // the gate tile of this workgroup is one contiguous 256 x 128 block
-            const uint16_t* gt = p.G + ((size_t)mt * (p.N / kGateTileCols) + nt) * (TM * kGateTileCols);
-            const bool full = m0 + TM <= p.M;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint16_t gv[NJ / 2][16];
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
-#pragma unroll
-                    for (int j = 0; j < NJ / 2; ++j)
-                        gv[j][v] = (full || m0 + rt < p.M) ? gt[rt * kGateTileCols + wn * GB + j * 32 + r32]
-                                                           : kGateDropped;
-                }
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
-                    const int64_t m = m0 + rt;
-#pragma unroll
-                    for (int j = 0; j < NJ / 2; ++j) {
-                        const int n = n0 + wn * GB + j * 32 + r32;
-                        const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
-                        const bool keep = gv[j][v] != kGateDropped;
-                        const float sg = p.gate ? sigmoidf_dev(u)
-                                                : (float)__builtin_bit_cast(_Float16, gv[j][v]);
-                        if (full || m < p.M) p.Cb[m * p.N + n] = keep ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
-                    }
-                }
             }
             return;
         }
@@ -560,8 +489,8 @@ static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int
     constexpr int WN = SFFN_GEMM256_WN;
     const int m_tiles = (int)((p.M + TM - 1) / TM);
     const int n_tiles = (p.N + (EPI == EPI_GATEUP ? TN / 2 : TN) - 1) / (EPI == EPI_GATEUP ? TN / 2 : TN);
-    xlaunch(events, stage, k_gemm256<EPI, WN>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0,
-            s, p, m_tiles, n_tiles);
+    xlaunch(events, stage, k_gemm256<EPI, WN>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0, s, p,
+            m_tiles, n_tiles);
 }
 
 template <int EPI>

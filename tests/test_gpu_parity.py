@@ -288,6 +288,23 @@ def test_forward_long_context_chunks(full_layer, ffn_full):
     assert torch.equal(y2.view(torch.int16), y[C // 2:C // 2 + C].view(torch.int16))
 
 
+def test_forward_many_tiles_ragged(full_layer, ffn_full):
+    """2500 tokens: more 256 x 128 gate/up tiles than compute units (each
+    workgroup walks several tiles) and a ragged last row tile. Sampled rows
+    against the oracle, and the first 256 rows equal a separate 256-token
+    call (one tile per workgroup) bit for bit."""
+    T = 2500
+    x = wl.make_tokens(wl.FULL, T, seed=2500, outlier_frac=0.01)
+    xd = dev(x)
+    y, mask, logits = ffn_full(xd, return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 1023, 2303, 2304, 2305, 2450, 2499]
+    check_forward(full_layer, x, y, mask, logits, tokens=rows, bias=False)
+    y256 = ffn_full(xd[:256])
+    torch.cuda.synchronize()
+    assert torch.equal(y256.view(torch.int16), y[:256].view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 5, 64, 200, 300])
 @pytest.mark.parametrize("gate", ["pred", "silu"])
 def test_forward_mid_shapes(mid_layer, T, gate):
