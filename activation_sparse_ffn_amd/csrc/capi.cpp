@@ -247,6 +247,10 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const PackedLayout& L = h->L;
+    // Every channel kept with the silu gate (the dense fallback): the mask is
+    // all ones and the gate comes from u, so the predictor only runs when the
+    // logits are asked for.
+    const bool need_pred = !(c.gate == SFFN_GATE_SILU && c.keep == c.bank && logits_out == nullptr);
     void* pk = h->packed;
     const float* bias = h->has_bias ? at<float>(pk, L.bias) : nullptr;
     hipError_t he;
@@ -265,6 +269,8 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.pk = at<float>(workspace, w.pk);
         a.h = at<float>(workspace, w.h);
         a.partial = at<float>(workspace, w.partial);
+        a.need_pred = need_pred;
+        a.mask_requested = mask_out != nullptr;
         a.events = h->profiling ? h->events : nullptr;
         he = sffn::launch_gather_forward(a, s);
     } else {
@@ -285,6 +291,8 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
                            ? at<uint16_t>(workspace, w.gate) : nullptr;
         a.z_partial = (!use_skinny(c, T) && sffn::z_splits(T, c.d) > 1) ? at<float>(workspace, w.zpart)
                                                                          : nullptr;
+        a.need_pred = need_pred;
+        a.mask_requested = mask_out != nullptr;
         a.events = h->profiling ? h->events : nullptr;
         he = use_skinny(c, T) ? sffn::launch_skinny_forward(a, at<float>(workspace, w.partial), s)
                               : sffn::launch_mfma_forward(a, s);
@@ -332,6 +340,10 @@ const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
     static const char* mfma[] = {"pred1_gemm", "pred2_gemm", "bank_topk", "gateup_gemm", "down_gemm"};
     static const char* mfma_fused[] = {"pred1_gemm", "pred2_topk_gemm", "none", "gateup_gemm", "down_gemm"};
     if (!h || i < 0 || i >= sffn::kStages) return nullptr;
+    // the dense fallback skips the predictor (and top-k) stages unless the
+    // logits are asked for
+    const bool dense_silu = h->cfg.gate == SFFN_GATE_SILU && h->cfg.keep == h->cfg.bank;
+    if (dense_silu && i < (use_gather(h->cfg, T) ? 2 : 3)) return "none";
     if (!use_gather(h->cfg, T)) {
         const sffn_config_t& c = h->cfg;
         const bool fused = !use_skinny(c, T) && sffn::mfma_fused_topk(T, c.d, c.d_i, c.rank);

@@ -211,6 +211,7 @@ __device__ __forceinline__ uint64_t lowest_bits(uint64_t x, int n) {
 // channel first.
 template <typename Load>
 __device__ __forceinline__ uint64_t lane_select64(Load load, int keep) {
+    if (keep >= kBank) return ~0ull;
     float k[kBank];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {

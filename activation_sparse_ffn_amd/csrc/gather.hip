@@ -161,7 +161,8 @@ __global__ __launch_bounds__(256) void k_gateup(const E* __restrict__ x, const E
     const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= n_work) return;
     const unsigned t = (unsigned)w / (unsigned)d_s;
-    const int64_t j = ids[w];
+    // no id list: every channel, in order
+    const int64_t j = ids ? (int64_t)ids[w] : w - (int64_t)t * d_s;
     const E* xr = x + (size_t)t * d;
     const E* gr = Wg + j * d;
     const E* ur = Wu + j * d;
@@ -230,7 +231,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
         Raw<E> rw[16];
         float hv[16];
         const size_t base = (size_t)t * d_s + slot0;
-        if constexpr (EXACT) {
+        if (ids == nullptr) {
+            // every channel, in order: rows slot0 .. slot0 + 15
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (EXACT || i < n_rows) {
+                    hv[i] = h[base + i];
+                    rw[i].load(WdT + (size_t)(slot0 + i) * d + col);
+                }
+            }
+        } else if constexpr (EXACT) {
             // sixteen ids as two 16-byte words, made wave-uniform so that the
             // row addresses live in scalar registers and all 16 row loads
             // issue back to back
@@ -469,38 +479,50 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
     const int64_t T = a.T;
     const int nch = a.d / 8;
     const int rb = a.dt == Dt::BF16 ? 1 : 0;
-    if (nch % (256 * 2) == 0)
-        xlaunch(a.events, 0, k_pred1<E, 2, true>, dim3((unsigned)(T * a.rank)), dim3(256), 0, s, x,
-                static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
-    else
-        xlaunch(a.events, 0, k_pred1<E, 2, false>, dim3((unsigned)(T * a.rank)), dim3(256), 0, s, x,
-                static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
-    if constexpr (sizeof(E) == 2) {
-        if (fused_ok(a)) {
-            xlaunch(a.events, 1, k_bank_fused<16>, dim3((unsigned)(T * nb)), dim3(512), 0, s, x, a.z,
-                    static_cast<const E*>(a.B), a.bias, static_cast<const E*>(a.W_g),
-                    static_cast<const E*>(a.W_u), static_cast<const E*>(a.W_dT), a.rank, a.d_i,
-                    a.gate, a.mask, a.logits, a.partial);
-            const int col_blocks = (a.d + 31) / 32;
-            xlaunch(a.events, 2, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
-                    a.partial, static_cast<E*>(a.y), a.d, nb, col_blocks);
-            skip_stages(a.events, 3, s);
-            return hipGetLastError();
+    // every channel kept with the silu gate and no logits asked for: no
+    // predictor and no top-k; gate/up and down walk all channels in order
+    const bool dense = !a.need_pred;
+    const uint16_t* ids = dense ? nullptr : a.ids;
+    if (dense) {
+        skip_range(a.events, 0, 2, s);
+        if (a.mask_requested) {
+            const hipError_t e = launch_fill_mask(a.mask, T * nb, s);
+            if (e != hipSuccess) return e;
         }
+    } else {
+        if (nch % (256 * 2) == 0)
+            xlaunch(a.events, 0, k_pred1<E, 2, true>, dim3((unsigned)(T * a.rank)), dim3(256), 0, s, x,
+                    static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
+        else
+            xlaunch(a.events, 0, k_pred1<E, 2, false>, dim3((unsigned)(T * a.rank)), dim3(256), 0, s, x,
+                    static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
+        if constexpr (sizeof(E) == 2) {
+            if (fused_ok(a)) {
+                xlaunch(a.events, 1, k_bank_fused<16>, dim3((unsigned)(T * nb)), dim3(512), 0, s, x, a.z,
+                        static_cast<const E*>(a.B), a.bias, static_cast<const E*>(a.W_g),
+                        static_cast<const E*>(a.W_u), static_cast<const E*>(a.W_dT), a.rank, a.d_i,
+                        a.gate, a.mask, a.logits, a.partial);
+                const int col_blocks = (a.d + 31) / 32;
+                xlaunch(a.events, 2, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
+                        a.partial, static_cast<E*>(a.y), a.d, nb, col_blocks);
+                skip_stages(a.events, 3, s);
+                return hipGetLastError();
+            }
+        }
+        xlaunch(a.events, 1, k_pred2_topk<E>, dim3((unsigned)(T * nb)), dim3(256), 0, s, a.z,
+                static_cast<const E*>(a.B), a.bias, a.rank, a.d_i, a.keep, a.mask, a.logits, a.ids,
+                a.pk);
     }
-    xlaunch(a.events, 1, k_pred2_topk<E>, dim3((unsigned)(T * nb)), dim3(256), 0, s, a.z,
-            static_cast<const E*>(a.B), a.bias, a.rank, a.d_i, a.keep, a.mask, a.logits, a.ids,
-            a.pk);
     {
         const int64_t n = T * d_s;
         const dim3 grid((unsigned)((n + 3) / 4));
         if (nch % (64 * NC) == 0)
             xlaunch(a.events, 2, k_gateup<E, NC, true>, grid, dim3(256), 0, s, x,
-                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), a.ids, a.pk, a.h,
+                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), ids, a.pk, a.h,
                     a.d, d_s, n, a.gate);
         else
             xlaunch(a.events, 2, k_gateup<E, NC, false>, grid, dim3(256), 0, s, x,
-                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), a.ids, a.pk, a.h,
+                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), ids, a.pk, a.h,
                     a.d, d_s, n, a.gate);
     }
     const int groups = gather_groups(d_s);
@@ -509,10 +531,10 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
         const dim3 grid((unsigned)(T * groups * slices));
         if (a.d % kSlice == 0 && d_s % kGroup == 0)
             xlaunch(a.events, 3, k_down<E, true>, grid, dim3(256), 0, s,
-                    static_cast<const E*>(a.W_dT), a.ids, a.h, a.partial, a.d, d_s, groups, slices);
+                    static_cast<const E*>(a.W_dT), ids, a.h, a.partial, a.d, d_s, groups, slices);
         else
             xlaunch(a.events, 3, k_down<E, false>, grid, dim3(256), 0, s,
-                    static_cast<const E*>(a.W_dT), a.ids, a.h, a.partial, a.d, d_s, groups, slices);
+                    static_cast<const E*>(a.W_dT), ids, a.h, a.partial, a.d, d_s, groups, slices);
     }
     {
         const int col_blocks = (a.d + 31) / 32;

@@ -42,6 +42,7 @@ struct GemmParams {
     uint64_t* mask_w;    // [M, N/64]
     uint16_t* gate_w;    // fp16 gate tiles
     int keep;
+    int dense;           // EPI_GATEUP without gate tiles: every channel kept (silu gate)
 };
 
 constexpr int BM = 128, BN = 128, BK = 32;
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     // + 4 (lane >> 5); for gate/up, tile j < NJ / 2 holds u and tile
     // j + NJ / 2 holds v of channels n0 + wn GB + 32 j + (lane & 31)
     if constexpr (GU) {
-        if (gtile != nullptr) {
+        if (gtile != nullptr || p.dense) {
             // H = select(kept, s u v, 0) with the gate values of the LDS
             // copy of the gate tile, written over them in place (each
             // element is read and written by one lane); the bf16 tile then
@@ -440,7 +441,8 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
                     for (int v = 0; v < 16; ++v) {
                         const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
                         const float sg = p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g[v]);
-                        *e[v] = g[v] != kGateDropped ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                        const bool kept = p.dense || g[v] != kGateDropped;   // dense: no gate tile loaded
+                        *e[v] = kept ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
                     }
                 }
             __syncthreads();
@@ -524,7 +526,28 @@ int z_splits(int64_t T, int d) {
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     // the 256-wide tiles need K to be a multiple of 64 and enough rows to fill them
     const bool big = a.T >= 256 && a.d % 64 == 0 && a.d_i % 64 == 0;
+    const bool tiles = big && a.gate_tiles != nullptr && a.d_i % kGateTileCols == 0;
     GemmParams g{};
+    if (!a.need_pred) {
+        // every channel kept with the silu gate and no logits asked for: no
+        // predictor and no top-k. The 256-wide gate/up epilogue keeps every
+        // channel by itself; the mask is written when asked for or read.
+        skip_range(a.events, 0, 3, s);
+        if (a.mask_requested || !big) {
+            const hipError_t e = launch_fill_mask(a.mask, a.T * (a.d_i / kBank), s);
+            if (e != hipSuccess) return e;
+        }
+        g = GemmParams{};
+        g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;
+        g.mask = a.mask; g.gate = a.gate; g.dense = big ? 1 : 0;
+        if (big) gemm256<EPI_GATEUP>(g, s, a.events, 3);
+        else gemm<EPI_GATEUP>(g, s, a.events, 3);
+        g = GemmParams{};
+        g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
+        if (big) gemm256<EPI_BF16>(g, s, a.events, 4);
+        else gemm<EPI_BF16>(g, s, a.events, 4);
+        return hipGetLastError();
+    }
     // Z = bf16(X A^T)
     g.A = a.x; g.B0 = a.A; g.M = a.T; g.N = a.rank; g.K = a.d; g.Cb = a.z;
     const int zs = z_splits(a.T, a.d);
@@ -543,7 +566,6 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     }
     // P = Z B^T + bias
     g = GemmParams{};
-    const bool tiles = big && a.gate_tiles != nullptr && a.d_i % kGateTileCols == 0;
     if (tiles && mfma_fused_topk(a.T, a.d, a.d_i, a.rank)) {
         // P, bank top-k and gate tiles in one kernel; the logits reach HBM
         // only when the caller asked for them

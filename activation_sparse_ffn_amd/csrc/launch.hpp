@@ -24,6 +24,17 @@ inline void skip_stages(void* const* events, int from, hipStream_t s) {
         (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
 }
 
+// Records the start and stop events of stages [from, to) back to back, for
+// stages a call skips.
+inline void skip_range(void* const* events, int from, int to, hipStream_t s) {
+    if (!events) return;
+    for (int i = 2 * from; i < 2 * to; ++i)
+        (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+}
+
+// Every channel kept: n_words mask words of all ones.
+hipError_t launch_fill_mask(uint64_t* mask, int64_t n_words, hipStream_t s);
+
 template <typename F, typename... Args>
 inline void xlaunch(void* const* events, int stage, F kernel, dim3 grid, dim3 block,
                     uint32_t shmem, hipStream_t s, Args... args) {
@@ -64,6 +75,9 @@ struct GatherArgs {
     float* pk;                      // [T, d_s]        kept logits
     float* h;                       // [T, d_s]        kept activations
     float* partial;                 // [T, groups, d]  down partial sums
+    bool need_pred;                 // false: every channel kept with the silu gate
+                                    // and no logits asked for, so no predictor
+    bool mask_requested;            // mask points at the caller's mask_out
     void* const* events;            // null or 2 * kStages hipEvent_t
 };
 int gather_groups(int d_s);
@@ -89,6 +103,9 @@ struct MfmaArgs {
     uint16_t* gate_tiles;   // fp16 gate tiles (see launch_bank_topk) or null
     float* z_partial;       // [z_splits, T, rank] K-split partials of z, or null
     bool logits_requested;  // logits points at the caller's logits_out
+    bool need_pred;         // false: every channel kept with the silu gate and no
+                            // logits asked for, so no predictor and no top-k
+    bool mask_requested;    // mask points at the caller's mask_out
     void* const* events;    // null or 2 * kStages hipEvent_t
 };
 // K splits of predictor layer 1 on the MFMA path (1 = no split)

@@ -250,27 +250,35 @@ size_t skinny_partial_floats(int64_t T, int d, int rank, int d_i) {
 hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t s) {
     const int M = (int)a.T;
     SkinnyParams p{};
-    // Z = bf16(X A^T)
-    {
-        const int sp = k_splits(a.rank, a.d);
-        p = SkinnyParams{};
-        p.A = a.x; p.B0 = a.A; p.M = M; p.N = a.rank; p.K = a.d;
-        if (sp == 1) {
-            p.Cb = a.z;
-            skinny<SK_BF16, 1>(p, 1, s, a.events, 0, true);
-        } else {
-            p.partial = partial;
-            skinny<SK_PARTIAL, 1>(p, sp, s, a.events, 0, false);
-            sum_bf16(partial, a.z, sp, (int64_t)M * a.rank, s, a.events, 0);
+    if (!a.need_pred) {
+        // every channel kept with the silu gate and no logits asked for: no
+        // predictor and no top-k; the gate/up epilogue reads an all-ones mask
+        skip_range(a.events, 0, 3, s);
+        const hipError_t e = launch_fill_mask(a.mask, a.T * (a.d_i / kBank), s);
+        if (e != hipSuccess) return e;
+    } else {
+        // Z = bf16(X A^T)
+        {
+            const int sp = k_splits(a.rank, a.d);
+            p = SkinnyParams{};
+            p.A = a.x; p.B0 = a.A; p.M = M; p.N = a.rank; p.K = a.d;
+            if (sp == 1) {
+                p.Cb = a.z;
+                skinny<SK_BF16, 1>(p, 1, s, a.events, 0, true);
+            } else {
+                p.partial = partial;
+                skinny<SK_PARTIAL, 1>(p, sp, s, a.events, 0, false);
+                sum_bf16(partial, a.z, sp, (int64_t)M * a.rank, s, a.events, 0);
+            }
         }
+        // P = Z B^T + bias
+        p = SkinnyParams{};
+        p.A = a.z; p.B0 = a.B; p.M = M; p.N = a.d_i; p.K = a.rank; p.Cf = a.logits; p.bias = a.bias;
+        skinny<SK_F32_BIAS, 1>(p, 1, s, a.events, 1, true);
+        // mask
+        const hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2);
+        if (e != hipSuccess) return e;
     }
-    // P = Z B^T + bias
-    p = SkinnyParams{};
-    p.A = a.z; p.B0 = a.B; p.M = M; p.N = a.d_i; p.K = a.rank; p.Cf = a.logits; p.bias = a.bias;
-    skinny<SK_F32_BIAS, 1>(p, 1, s, a.events, 1, true);
-    // mask
-    hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2);
-    if (e != hipSuccess) return e;
     // H = select(m, s u v, 0)
     p = SkinnyParams{};
     p.A = a.x; p.B0 = a.W_g; p.B1 = a.W_u; p.M = M; p.N = a.d_i; p.K = a.d; p.Cb = a.h;

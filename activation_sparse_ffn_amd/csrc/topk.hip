@@ -120,6 +120,17 @@ __global__ __launch_bounds__(256) void k_bank_topk_lanes(const float* __restrict
     }
 }
 
+__global__ __launch_bounds__(256) void k_fill_mask(uint64_t* __restrict__ mask, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) mask[i] = ~0ull;
+}
+
+hipError_t launch_fill_mask(uint64_t* mask, int64_t n_words, hipStream_t s) {
+    if (mask == nullptr || n_words <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_mask, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, s, mask, n_words);
+    return hipGetLastError();
+}
+
 size_t gate_tiles_bytes(int64_t T, int d_i) {
     return (size_t)((T + kGateTileRows - 1) / kGateTileRows) * kGateTileRows * d_i * 2;
 }

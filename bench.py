@@ -28,6 +28,7 @@ gives the roofline entry. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -59,6 +60,10 @@ def parse():
                     help="budget of the oracle's bounded CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--keep", type=int, default=16,
+                    help="channels kept per 64-channel bank (64: the dense modes)")
+    ap.add_argument("--gate", choices=["pred", "silu"], default="pred",
+                    help="gate of the kept channels: sigmoid of the predictor logit or of u")
     return ap.parse_args()
 
 
@@ -66,15 +71,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic(wl_name, shape, T, masks_union_frac=None):
+def algorithmic(wl_name, shape, T, masks_union_frac=None, gate="pred"):
     """Algorithmic bytes and flops of one step.
 
     Weights touched per token (bf16): predictor A and B in full, and for each
-    of the d_s kept channels one row of W_g, one of W_u and one of W_d^T.
+    of the d_s kept channels one row of W_g, one of W_u and one of W_d^T. The
+    dense fallback (every channel kept, SiLU gate) needs no predictor.
     """
     d, d_i, r, ds = shape.d, shape.d_i, shape.rank, shape.d_s
     e = 2
-    pred = (r * d + d_i * r) * e
+    no_pred = gate == "silu" and shape.keep == shape.bank
+    pred = 0 if no_pred else (r * d + d_i * r) * e
+    if no_pred:
+        r = 0
     row = d * e
     if wl_name == "decode":
         gateup = 2 * ds * row * T
@@ -105,7 +114,7 @@ def profiled_traffic(kernel):
     return None
 
 
-def cpu_baseline(layer, T, budget_s):
+def cpu_baseline(layer, T, budget_s, keep=16, gate="pred"):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
     import oracle as o
@@ -122,7 +131,7 @@ def cpu_baseline(layer, T, budget_s):
     while time.perf_counter() - t0 < budget_s:
         x = wl.make_tokens(layer.shape, chunk, seed=seed)
         seed += 1
-        o.forward(x, layer.A, layer.B, layer.W_g, layer.W_u, layer.W_d, bias=layer.bias)
+        o.forward(x, layer.A, layer.B, layer.W_g, layer.W_u, layer.W_d, bias=layer.bias, keep=keep, gate=gate)
         n_tok += chunk
     el = time.perf_counter() - t0
     return dict(value=n_tok / el, unit="tokens/s", cores=int(cores), kind="oracle",
@@ -232,7 +241,7 @@ def main():
     cfg = WORKLOADS[args.workload]
     T = cfg["T"]
     n_layers = args.layers or cfg["layers"]
-    shape = wl.FULL
+    shape = dataclasses.replace(wl.FULL, keep=args.keep)
     K, W = args.steps, args.warmup
 
     def dev(a):
@@ -246,7 +255,7 @@ def main():
     for li in range(n_layers):
         L = wl.make_layer(shape, seed=li, bias_var=0.5 if cfg["bias"] else None)
         ffns.append(sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B),
-                                   dev(L.bias) if cfg["bias"] else None))
+                                   dev(L.bias) if cfg["bias"] else None, keep=args.keep, gate=args.gate))
         if li == 0:
             layer0 = L
         del L
@@ -315,7 +324,7 @@ def main():
             w = m.cpu().numpy().view(np.uint64)
             fr.append(np.bitwise_count(np.bitwise_or.reduce(w, axis=0)).sum() / shape.d_i)
         union_frac = float(np.mean(fr))
-    alg = algorithmic(args.workload, shape, T, union_frac)
+    alg = algorithmic(args.workload, shape, T, union_frac, args.gate)
 
     # ---- per-stage durations (kernel start/stop events) ---------------------
     n_ev = 2 * sffn.SFFN_STAGES
@@ -384,7 +393,7 @@ def main():
         "data": "synthetic (seeded N(0, 1/fan_in) weights, N(0, 1) tokens)",
         "config": {
             "workload": f"{args.workload}: {T} token(s) per step, d=4096, d_i=14336, rank=448, "
-                        f"keep 16 of 64 per bank, {n_layers} layers rotated",
+                        f"keep {args.keep} of 64 per bank, gate {args.gate}, {n_layers} layers rotated",
             "tokens_per_step": T, "layers_rotated": n_layers, "graph": graph is not None,
         },
         "step_hbm_gbs": round(alg["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
@@ -397,7 +406,7 @@ def main():
         out["executed_tflops"] = round(alg["executed_flops"] / (ms_per_step * 1e-3) / 1e12, 1)
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
-        out["cpu_baseline"] = cpu_baseline(layer0, T, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(layer0, T, args.cpu_seconds, args.keep, args.gate)
     print(json.dumps(out), flush=True)
 
 

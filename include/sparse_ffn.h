@@ -112,6 +112,13 @@ size_t sparse_ffn_workspace_size(sffn_handle_t h, int64_t T);
  *   logits_out [T, d_i] fp32 or NULL: the predictor logits p
  *   workspace  device scratch of >= sparse_ffn_workspace_size(h, T) bytes,
  *              not shared with a concurrent call
+ * keep = 64 keeps every channel: with SFFN_GATE_PREDICTOR it is the
+ * predictor-gated dense FFN of the training recipe's fourth stage
+ * ("Continual LLM Upcycling", Methodologie > 2. Trainingsrecept); with
+ * SFFN_GATE_SILU it is the plain dense SwiGLU, one reading of the single-
+ * layer dense fallback (Belangrijkste Bijdragen, item 3). In the latter the
+ * predictor runs only when logits_out is given; mask_out (if given) is all
+ * ones.
  * T == 0 returns SFFN_OK and enqueues nothing. Calls on different streams
  * may overlap if each has its own workspace and outputs. */
 sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T,
@@ -142,9 +149,10 @@ sffn_status_t bank_topk(const float* logits, int64_t T, int32_t d_i,
 sffn_status_t sparse_ffn_set_stage_events(sffn_handle_t h, void* const* events,
                                           int32_t n_events);
 
-/* Name of stage i (0 <= i < SFFN_STAGES) of a forward of T tokens, e.g.
- * "gateup"; "none" for a stage the chosen path does not have (its two events
- * are recorded back to back); NULL when out of range. */
+/* Name of stage i (0 <= i < SFFN_STAGES) of a forward of T tokens that asks
+ * for no logits, e.g. "gateup"; "none" for a stage the chosen path does not
+ * have (its two events are recorded back to back; with keep = 64 and the silu
+ * gate these are the predictor and top-k stages); NULL when out of range. */
 const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i);
 
 /* Free the handle (host memory only; `packed` stays the caller's). */

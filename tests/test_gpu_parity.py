@@ -327,6 +327,30 @@ def test_keep_all_channels_is_dense(mid_layer, T, gate):
     check_forward(mid_layer, x, y, mask, logits, bias=True, keep=64, gate=gate)
 
 
+@pytest.mark.parametrize("T", [1, 3, 32, 300])
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_dense_modes_full(full_layer, T, gate):
+    """keep = 64: with the predictor gate, the predictor-gated dense FFN; with
+    the silu gate, the plain dense SwiGLU, for which no predictor or top-k
+    runs unless the logits are asked for. y does not depend on asking for the
+    mask or the logits (bit for bit), the mask is all ones, and sampled rows
+    match the oracle (T = 1, 3: gather path; 32: skinny; 300: 256-wide
+    tiles)."""
+    ffn = make_ffn(full_layer, bias=True, keep=64, gate=gate)
+    x = wl.make_tokens(wl.FULL, T, seed=640 + T)
+    xd = dev(x)
+    y0 = ffn(xd)
+    y1, m1 = ffn(xd, return_mask=True)
+    y2, m2, lg = ffn(xd, return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y0), host(y2))
+    np.testing.assert_array_equal(host(y1), host(y2))
+    assert (words(m1) == np.uint64(0xFFFFFFFFFFFFFFFF)).all()
+    np.testing.assert_array_equal(words(m1), words(m2))
+    rows = None if T <= 4 else [0, 1, T // 2, T - 1]
+    check_forward(full_layer, x, y2, m2, lg, tokens=rows, bias=True, keep=64, gate=gate)
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_gate_silu_full(full_layer, T):
     ffn = make_ffn(full_layer, bias=True, gate="silu")
