@@ -48,18 +48,28 @@ struct GemmParams {
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LDS_STRIDE = BK + 8;   // elements; 80-byte rows keep 16-byte alignment
 
-template <int EPI>
+// LDS slab layout shared by the LDS-direct loops: a slab holds rows of 64
+// bf16 (128 bytes, eight 16-byte chunks); chunk g of row r sits in slot
+// g ^ ((r >> 1) & 7), which spreads a fragment read over all LDS banks.
+__device__ __forceinline__ int slab_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int slab_off(int r, int g) { return r * 128 + ((g ^ slab_swz(r)) << 4); }
+
+constexpr int TKD = 64;                  // K step of the LDS-direct loops
+constexpr int SLAB128 = BM * TKD * 2;    // one 128-row slab: 16 KB
+
+// DMA: the LDS-direct loop (K range a multiple of 64): slabs go global ->
+// LDS with global_load_lds_dwordx4 into two buffers (separate arrays, loop
+// unrolled by two), fragment reads interleaved one per MFMA with the
+// sub-step before, and the barrier before each step's last sub-step. Else
+// the register-staged loop with 32-wide K steps.
+template <int EPI, bool DMA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_TOPK ? 2 : 1))) void k_gemm(const GemmParams p) {
     constexpr int NB = (EPI == EPI_GATEUP) ? 2 : 1;
-    constexpr int STAGE_BYTES = (BM + NB * BN) * LDS_STRIDE * 2;
-    constexpr int TILE_BYTES = EPI == EPI_TOPK ? BM * BN * 4 : 0;     // fp32 logits tile
-    __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > TILE_BYTES ? STAGE_BYTES : TILE_BYTES];
-    uint16_t* const As = reinterpret_cast<uint16_t*>(smem);
-    auto BS = [&](int b) { return As + (BM + b * BN) * LDS_STRIDE; };
-
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 1, wn = wv & 1;
+    const int r32 = lane & 31, hk = lane >> 5;
     const int n_tiles = (p.N + BN - 1) / BN;
     const int64_t mt = blockIdx.x % ((p.M + BM - 1) / BM);
     const int nt = (int)(blockIdx.x / ((p.M + BM - 1) / BM));
@@ -68,37 +78,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
     const int n0 = nt * BN;
     const int kn = EPI == EPI_PARTIAL ? p.kn : p.K;      // this workgroup's K range
     const int kb = EPI == EPI_PARTIAL ? (int)blockIdx.y * p.kn : 0;
-
-    // global -> register staging: each thread moves 2 chunks of 8 elements
-    // per operand tile (128 rows x 4 chunks)
-    uint4 ra[2], rb[NB][2];
-    auto load_tiles = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 2, kc = (c & 3) * 8;
-            const int64_t gm = m0 + row;
-            ra[i] = (gm < p.M) ? *reinterpret_cast<const uint4*>(p.A + gm * p.K + k0 + kc)
-                               : make_uint4(0, 0, 0, 0);
-            const int gn = n0 + row;
-            rb[0][i] = (gn < p.N) ? *reinterpret_cast<const uint4*>(p.B0 + (int64_t)gn * p.K + k0 + kc)
-                                  : make_uint4(0, 0, 0, 0);
-            if constexpr (NB == 2)
-                rb[1][i] = (gn < p.N) ? *reinterpret_cast<const uint4*>(p.B1 + (int64_t)gn * p.K + k0 + kc)
-                                      : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_tiles = [&]() {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 2, kc = (c & 3) * 8;
-            *reinterpret_cast<uint4*>(&As[row * LDS_STRIDE + kc]) = ra[i];
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                *reinterpret_cast<uint4*>(&BS(b)[row * LDS_STRIDE + kc]) = rb[b][i];
-        }
-    };
 
     f32x16 acc[NB][2][2];
 #pragma unroll
@@ -109,39 +88,169 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
-
-    const int kt_n = kn / BK;
-    load_tiles(kb);
-    for (int kt = 0; kt < kt_n; ++kt) {
-        store_tiles();
-        __syncthreads();
-        if (kt + 1 < kt_n) load_tiles(kb + (kt + 1) * BK);
+    auto mma = [&](const bf16x8 (&af)[2], const bf16x8 (&bfr)[NB][2]) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            const int ko = kk + 8 * (lane >> 5);
-            bf16x8 af[2], bfr[NB][2];
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
+    };
+    // EPI_TOPK: the fp32 logit tile as 256 bank-rows of 256 bytes, rows
+    // 0..127 in `tile_lo`, 128..255 in `tile_hi` (the freed staging buffers)
+    char* tile_lo;
+    char* tile_hi;
+
+    if constexpr (DMA) {
+        __shared__ __attribute__((aligned(16))) char buf0[(1 + NB) * SLAB128];
+        __shared__ __attribute__((aligned(16))) char buf1[(1 + NB) * SLAB128];
+        // per-thread fetch rows: chunk c = tid + 256 i -> row c / 8, slot c % 8
+        // (lane l of a wave lands at base + 16 l). Rows past M or N read row
+        // 0: their results are never stored.
+        const int fs = tid & 7;
+        const uint16_t* asrc[4];
+        const uint16_t* bsrc[NB][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 3) + 32 * i;
+            const int gch = fs ^ slab_swz(r);
+            const int64_t m = m0 + r;
+            asrc[i] = p.A + (m < p.M ? m : 0) * p.K + kb + 8 * gch;
+            const int n = n0 + r;
+            const int64_t nr = n < p.N ? n : 0;
+            bsrc[0][i] = p.B0 + nr * p.K + kb + 8 * gch;
+            if constexpr (NB == 2) bsrc[1][i] = p.B1 + nr * p.K + kb + 8 * gch;
+        }
+        auto fetch = [&](int k0, char* dst) {
+            char* wbase = dst + wv * (kWave * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(asrc[i] + k0),
+                                                 (__attribute__((address_space(3))) void*)(wbase + i * 4096), 16, 0, 0);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    __builtin_amdgcn_global_load_lds(
+                        (const __attribute__((address_space(1))) void*)(bsrc[b][i] + k0),
+                        (__attribute__((address_space(3))) void*)(wbase + (1 + b) * SLAB128 + i * 4096), 16, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto frags = [&](const char* S, int sub, bf16x8 (&af)[2], bf16x8 (&bfr)[NB][2]) {
+            const int gch = 2 * sub + hk;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(S + slab_off(wm * 64 + i * 32 + r32, gch));
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bfr[b][j] = *reinterpret_cast<const bf16x8*>(S + (1 + b) * SLAB128 +
+                                                                  slab_off(wn * 64 + j * 32 + r32, gch));
+        };
+        auto landed = [&]() {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        auto interleave = [&]() {
+            constexpr int R = 2 + 2 * NB, M = 4 * NB;
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (M > R) __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        const int kt_n = kn / TKD;
+        bf16x8 xa[2], xb[NB][2], ya[2], yb[NB][2];
+        auto step = [&](char* cur, const char* nxt, int kt) {
+            mma(xa, xb); frags(cur, 1, ya, yb); interleave();
+            mma(ya, yb); frags(cur, 2, xa, xb); interleave();
+            mma(xa, xb); frags(cur, 3, ya, yb); interleave();
+            landed();                               // slab kt + 1 is in LDS, `cur` is free
+            if (kt + 2 < kt_n) fetch((kt + 2) * TKD, cur);
+            mma(ya, yb);
+            frags(nxt, 0, xa, xb);                  // after the last step: stale, unused
+            interleave();
+        };
+        fetch(0, buf0);
+        landed();
+        if (kt_n > 1) fetch(TKD, buf1);
+        frags(buf0, 0, xa, xb);
+        int kt = 0;
+        for (; kt + 2 <= kt_n; kt += 2) {
+            step(buf0, buf1, kt);
+            step(buf1, buf0, kt + 1);
+        }
+        if (kt < kt_n) step(buf0, buf1, kt);
+        __syncthreads();                           // every wave is done with the buffers
+        tile_lo = buf0;
+        tile_hi = buf1;
+    } else {
+        constexpr int STAGE_BYTES = (BM + NB * BN) * LDS_STRIDE * 2;
+        constexpr int TILE_BYTES = EPI == EPI_TOPK ? BM * BN * 4 : 0;     // fp32 logits tile
+        __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > TILE_BYTES ? STAGE_BYTES : TILE_BYTES];
+        uint16_t* const As = reinterpret_cast<uint16_t*>(smem);
+        auto BS = [&](int b) { return As + (BM + b * BN) * LDS_STRIDE; };
+        // global -> register staging: each thread moves 2 chunks of 8 elements
+        // per operand tile (128 rows x 4 chunks)
+        uint4 ra[2], rb[NB][2];
+        auto load_tiles = [&](int k0) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int row = wm * 64 + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const bf16x8*>(&As[row * LDS_STRIDE + ko]);
+                const int c = tid + 256 * i;
+                const int row = c >> 2, kc = (c & 3) * 8;
+                const int64_t gm = m0 + row;
+                ra[i] = (gm < p.M) ? *reinterpret_cast<const uint4*>(p.A + gm * p.K + k0 + kc)
+                                   : make_uint4(0, 0, 0, 0);
+                const int gn = n0 + row;
+                rb[0][i] = (gn < p.N) ? *reinterpret_cast<const uint4*>(p.B0 + (int64_t)gn * p.K + k0 + kc)
+                                      : make_uint4(0, 0, 0, 0);
+                if constexpr (NB == 2)
+                    rb[1][i] = (gn < p.N) ? *reinterpret_cast<const uint4*>(p.B1 + (int64_t)gn * p.K + k0 + kc)
+                                          : make_uint4(0, 0, 0, 0);
             }
+        };
+        auto store_tiles = [&]() {
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int i = 0; i < 2; ++i) {
+                const int c = tid + 256 * i;
+                const int row = c >> 2, kc = (c & 3) * 8;
+                *reinterpret_cast<uint4*>(&As[row * LDS_STRIDE + kc]) = ra[i];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int row = wn * 64 + j * 32 + (lane & 31);
-                    bfr[b][j] = *reinterpret_cast<const bf16x8*>(&BS(b)[row * LDS_STRIDE + ko]);
+                for (int b = 0; b < NB; ++b)
+                    *reinterpret_cast<uint4*>(&BS(b)[row * LDS_STRIDE + kc]) = rb[b][i];
+            }
+        };
+        const int kt_n = kn / BK;
+        load_tiles(kb);
+        for (int kt = 0; kt < kt_n; ++kt) {
+            store_tiles();
+            __syncthreads();
+            if (kt + 1 < kt_n) load_tiles(kb + (kt + 1) * BK);
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 16) {
+                const int ko = kk + 8 * hk;
+                bf16x8 af[2], bfr[NB][2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = wm * 64 + i * 32 + r32;
+                    af[i] = *reinterpret_cast<const bf16x8*>(&As[row * LDS_STRIDE + ko]);
                 }
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j],
-                                                                               acc[b][i][j], 0, 0, 0);
+                    for (int j = 0; j < 2; ++j) {
+                        const int row = wn * 64 + j * 32 + r32;
+                        bfr[b][j] = *reinterpret_cast<const bf16x8*>(&BS(b)[row * LDS_STRIDE + ko]);
+                    }
+                mma(af, bfr);
+            }
+            __syncthreads();
         }
-        __syncthreads();
+        tile_lo = smem;
+        tile_hi = smem + 128 * 256;
     }
 
     // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5)
@@ -150,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
         // logits (+ bias) into LDS as 256 bank-rows q = 2 row + (col >> 6) of
         // 256 bytes, 16-byte chunks swizzled by q; the staging buffers are free
         // (the K loop ended on a barrier)
-        char* tile = smem;
+        auto tile_row = [&](int q) { return (q < 128 ? tile_lo : tile_hi) + (q & 127) * 256; };
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -162,7 +271,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
                 for (int v = 0; v < 16; ++v) {
                     const int row = wm * 64 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * (lane >> 5);
                     const int q = 2 * row + (col >> 6), c64 = col & 63;
-                    *reinterpret_cast<float*>(tile + q * 256 + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
+                    *reinterpret_cast<float*>(tile_row(q) + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
                         acc[0][i][j][v] + bj;
                 }
             }
@@ -172,7 +281,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
         const int row = q >> 1, bsel = q & 1;
         const int64_t t = m0 + row;
         const int j0 = n0 + bsel * kBank;
-        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(tile + q * 256 + ((c ^ (q & 15)) << 4)); };
+        const char* trow = tile_row(q);
+        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(trow + ((c ^ (q & 15)) << 4)); };
         const uint64_t sel = lane_select64(ld, p.keep);
         if (t >= p.M || j0 >= p.N) return;
         p.mask_w[t * nb64 + j0 / kBank] = sel;
@@ -249,8 +359,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
 
-__device__ __forceinline__ int slab_swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int slab_off(int r, int g) { return r * 128 + ((g ^ slab_swz(r)) << 4); }
 
 template <int EPI, int WN>
 __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
@@ -499,7 +607,10 @@ template <int EPI>
 static void gemm(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
     const int64_t mt = (p.M + BM - 1) / BM;
     const int64_t nt = (p.N + BN - 1) / BN;
-    xlaunch(events, stage, k_gemm<EPI>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, p);
+    if (p.K % TKD == 0)
+        xlaunch(events, stage, k_gemm<EPI, true>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, p);
+    else
+        xlaunch(events, stage, k_gemm<EPI, false>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, p);
 }
 
 // Sum of K-split partials in a fixed order, rounded to bf16.
@@ -556,8 +667,12 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
         const int64_t tiles = ((a.T + BM - 1) / BM) * ((a.rank + BN - 1) / BN);
         hipEvent_t e0 = a.events ? static_cast<hipEvent_t>(a.events[0]) : nullptr;
         hipEvent_t e1 = a.events ? static_cast<hipEvent_t>(a.events[1]) : nullptr;
-        hipExtLaunchKernelGGL(k_gemm<EPI_PARTIAL>, dim3((unsigned)tiles, (unsigned)zs), dim3(256), 0, s,
-                              e0, nullptr, 0u, g);
+        if (g.kn % TKD == 0)
+            hipExtLaunchKernelGGL(k_gemm<EPI_PARTIAL, true>, dim3((unsigned)tiles, (unsigned)zs), dim3(256), 0,
+                                  s, e0, nullptr, 0u, g);
+        else
+            hipExtLaunchKernelGGL(k_gemm<EPI_PARTIAL, false>, dim3((unsigned)tiles, (unsigned)zs), dim3(256), 0,
+                                  s, e0, nullptr, 0u, g);
         const int64_t n = a.T * (int64_t)a.rank;
         hipExtLaunchKernelGGL(k_sum_splits_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                               nullptr, e1, 0u, (const float*)a.z_partial, a.z, zs, n);
