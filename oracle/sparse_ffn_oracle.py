@@ -37,6 +37,12 @@ Readings where the pages are silent (each one is listed in the design doc):
   h_j = m_j * sigma(u_j) * u_j * v_j ("silu");
 * y is returned in float64; callers compare the GPU's y after widening.
 
+It also computes the Dense-4x baseline the pages compare against (same
+summary, Resultaten: naive 4x sparsity applied post hoc from activation
+amplitude): gate and up run dense, the per-bank top-k ranks the amplitude
+|SiLU(u) * v| of every channel (rounded to fp32, the precision the decision is
+taken in), and only the kept channels enter the down projection.
+
 Every function here is pinned by a CPU test (tests/test_oracle_*.py) against
 closed forms, hand-worked examples, brute force or library routines.
 """
@@ -49,7 +55,7 @@ import numpy as np
 __all__ = [
     "widen", "round_to_bf16", "bf16_bits_of", "sigmoid", "predictor_logits",
     "bank_topk_mask", "mask_to_words", "words_to_mask", "sparse_swiglu",
-    "forward", "logit_gap",
+    "forward", "logit_gap", "amplitude_forward",
 ]
 
 
@@ -264,3 +270,41 @@ def logit_gap(p: np.ndarray, bank: int = 64, keep: int = 16) -> np.ndarray:
     if keep >= bank:
         return np.zeros(v.shape[:2])
     return v[..., keep - 1] - v[..., keep]
+
+
+# ----------------------------------------------------------------------------
+# Dense-4x baseline (Resultaten: naive post-hoc 4x sparsity from activation
+# amplitude; no predictor)
+# ----------------------------------------------------------------------------
+
+def amplitude_forward(x, W_g, W_u, W_d, bank: int = 64, keep: int = 16,
+                      mask_in: Optional[np.ndarray] = None,
+                      tokens: Optional[Sequence[int]] = None) -> dict:
+    """Post-hoc amplitude sparsity for the selected tokens: u = x W_g^T and
+    v = x W_u^T over every channel, a = sigma(u) * u * v, the bank top-k of
+    |fp32(a)| gives the mask, h = a on kept channels (0 elsewhere) and y sums
+    h[j] * W_d[:, j] over the kept channels only.
+
+    ``mask_in`` (uint64 words) replaces the amplitude top-k (mask-pinned
+    mode). Returns the amplitudes ``a`` (float64, fp32-rounded), ``score`` =
+    |a| as ranked, the mask, its words, h and y.
+    """
+    xs = np.asarray(x)
+    rows = np.arange(xs.shape[0]) if tokens is None else np.asarray(tokens)
+    X = widen(xs[rows])
+    u = X @ widen(W_g).T
+    v = X @ widen(W_u).T
+    a = (sigmoid(u) * u * v).astype(np.float32).astype(np.float64)
+    score = np.abs(a)
+    if mask_in is None:
+        m = bank_topk_mask(score, bank, keep)
+    else:
+        m = words_to_mask(np.asarray(mask_in)[rows], bank)
+    Wd = np.asarray(W_d)
+    d = Wd.shape[0]
+    h = np.where(m, a, 0.0)
+    y = np.zeros((len(rows), d), dtype=np.float64)
+    for n in range(len(rows)):
+        S = np.flatnonzero(m[n])
+        y[n] = widen(Wd[:, S]) @ a[n, S]
+    return dict(a=a, score=score, mask=m, words=mask_to_words(m, bank), h=h, y=y, tokens=rows)
