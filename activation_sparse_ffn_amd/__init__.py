@@ -31,7 +31,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 
 SFFN_OK, SFFN_ERR_INVALID_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = range(5)
 SFFN_F32, SFFN_BF16 = 0, 1
-GATES = {"pred": 0, "silu": 1}
+GATES = {"pred": 0, "silu": 1, "amplitude": 2}
 
 EXPORTED_SYMBOLS = (
     "sparse_ffn_packed_size", "sparse_ffn_create", "sparse_ffn_workspace_size",
@@ -149,23 +149,29 @@ class SparseFFN:
     buffer the object owns; the originals may be dropped afterwards.
     """
 
-    def __init__(self, W_g, W_u, W_d, A, B, bias=None, keep: int = 16, gate: str = "pred"):
+    def __init__(self, W_g, W_u, W_d, A=None, B=None, bias=None, keep: int = 16, gate: str = "pred"):
+        """gate: "pred" (sigmoid of the predictor logit), "silu" (sigmoid of
+        u) or "amplitude" (the Dense-4x post-hoc baseline: no predictor, the
+        mask ranks |SiLU(u) v|; A and B may then be None)."""
         self._lib = load_library()
-        _need_gpu(W_g, W_u, W_d, A, B, bias)
+        if gate not in GATES:
+            raise ValueError("gate must be 'pred', 'silu' or 'amplitude'")
+        if (A is None or B is None) and gate != "amplitude":
+            raise ValueError("the predictor weights A and B are needed unless gate='amplitude'")
+        _need_gpu(*(t for t in (W_g, W_u, W_d, A, B, bias) if t is not None))
         dt = W_g.dtype
         if dt not in (torch.bfloat16, torch.float32):
             raise ValueError("weights must be bfloat16 or float32")
-        if any(t.dtype != dt for t in (W_u, W_d, A, B)):
+        if any(t.dtype != dt for t in (W_u, W_d, A, B) if t is not None):
             raise ValueError("all weights must share one dtype")
         if bias is not None and bias.dtype != torch.float32:
             raise ValueError("bias must be float32")
         d_i, d = W_g.shape
-        rank = A.shape[0]
-        if W_u.shape != (d_i, d) or W_d.shape != (d, d_i) or A.shape != (rank, d) \
-                or B.shape != (d_i, rank) or (bias is not None and bias.shape != (d_i,)):
+        rank = A.shape[0] if A is not None else 32
+        if W_u.shape != (d_i, d) or W_d.shape != (d, d_i) \
+                or (A is not None and A.shape != (rank, d)) or (B is not None and B.shape != (d_i, rank)) \
+                or (bias is not None and bias.shape != (d_i,)):
             raise ValueError("inconsistent weight shapes")
-        if gate not in GATES:
-            raise ValueError("gate must be 'pred' or 'silu'")
         self.device = W_g.device
         self.dtype = dt
         self.cfg = Config(d, d_i, rank, 64, keep, SFFN_BF16 if dt == torch.bfloat16 else SFFN_F32,

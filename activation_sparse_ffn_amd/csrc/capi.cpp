@@ -61,7 +61,7 @@ sffn_status_t check_config(const sffn_config_t* c) {
         return fail(SFFN_ERR_INVALID_ARG, "rank must be a multiple of 32 (got %d)", c->rank);
     if (c->dtype != SFFN_F32 && c->dtype != SFFN_BF16)
         return fail(SFFN_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
-    if (c->gate != SFFN_GATE_PREDICTOR && c->gate != SFFN_GATE_SILU)
+    if (c->gate != SFFN_GATE_PREDICTOR && c->gate != SFFN_GATE_SILU && c->gate != SFFN_GATE_AMPLITUDE)
         return fail(SFFN_ERR_INVALID_ARG, "unknown gate %d", (int)c->gate);
     return SFFN_OK;
 }
@@ -91,14 +91,15 @@ bool use_gather(const sffn_config_t& c, int64_t T) {
 }
 
 struct WsGather {
-    size_t z, ids, pk, h, partial, mask, logits, total;
+    size_t z, ids, pk, h, partial, mask, amp, logits, total;
 };
 struct WsMfma {
     size_t z, logits, mask, h, partial, gate, zpart, total;
 };
 
 bool use_skinny(const sffn_config_t& c, int64_t T) {
-    return !use_gather(c, T) && T <= kSkinnyMaxTokens && c.rank % 64 == 0;
+    // (rank % 64 only matters for the predictor, which the amplitude gate has not)
+    return !use_gather(c, T) && T <= kSkinnyMaxTokens && (c.rank % 64 == 0 || c.gate == SFFN_GATE_AMPLITUDE);
 }
 
 WsGather ws_gather(const sffn_config_t& c, int64_t T) {
@@ -114,6 +115,8 @@ WsGather ws_gather(const sffn_config_t& c, int64_t T) {
     w.h = off;       off += align_up((size_t)T * ds * 4);
     w.partial = off; off += align_up((size_t)T * groups * c.d * 4);
     w.mask = off;    off += align_up((size_t)T * nb * 8);
+    w.amp = off;
+    if (c.gate == SFFN_GATE_AMPLITUDE) off += align_up((size_t)T * c.d_i * 4);
     w.logits = off;  // gather path writes logits only when asked
     w.total = off;
     return w;
@@ -173,10 +176,16 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* w_gate, co
     sffn_status_t st = check_config(cfg);
     if (st != SFFN_OK) return st;
     if (!out) return fail(SFFN_ERR_INVALID_ARG, "out is null");
+    // the amplitude gate (Dense-4x baseline) has no predictor: pred_a and
+    // pred_b may then be null (the packed predictor sections stay unset)
+    const bool amp = cfg->gate == SFFN_GATE_AMPLITUDE;
     const void* ptrs[] = {w_gate, w_up, w_down, pred_a, pred_b, packed};
     const char* names[] = {"w_gate", "w_up", "w_down", "pred_a", "pred_b", "packed"};
     for (int i = 0; i < 6; ++i) {
-        if (!ptrs[i]) return fail(SFFN_ERR_INVALID_ARG, "%s is null", names[i]);
+        if (!ptrs[i]) {
+            if (amp && (i == 3 || i == 4)) continue;
+            return fail(SFFN_ERR_INVALID_ARG, "%s is null", names[i]);
+        }
         if (!aligned16(ptrs[i])) return fail(SFFN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
     }
     if (pred_bias && !aligned16(pred_bias))
@@ -193,8 +202,8 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* w_gate, co
     auto cp = [&](size_t off, const void* src, size_t bytes) {
         if (he == hipSuccess) he = hipMemcpyAsync(at<char>(packed, off), src, bytes, hipMemcpyDeviceToDevice, s);
     };
-    cp(L.A, pred_a, r * d * e);
-    cp(L.B, pred_b, di * r * e);
+    if (pred_a) cp(L.A, pred_a, r * d * e);
+    if (pred_b) cp(L.B, pred_b, di * r * e);
     cp(L.Wg, w_gate, di * d * e);
     cp(L.Wu, w_up, di * d * e);
     cp(L.Wd, w_down, d * di * e);
@@ -250,7 +259,8 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
     // Every channel kept with the silu gate (the dense fallback): the mask is
     // all ones and the gate comes from u, so the predictor only runs when the
     // logits are asked for.
-    const bool need_pred = !(c.gate == SFFN_GATE_SILU && c.keep == c.bank && logits_out == nullptr);
+    const bool need_pred = !(c.gate == SFFN_GATE_SILU && c.keep == c.bank && logits_out == nullptr) &&
+                           c.gate != SFFN_GATE_AMPLITUDE;
     void* pk = h->packed;
     const float* bias = h->has_bias ? at<float>(pk, L.bias) : nullptr;
     hipError_t he;
@@ -269,6 +279,7 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.pk = at<float>(workspace, w.pk);
         a.h = at<float>(workspace, w.h);
         a.partial = at<float>(workspace, w.partial);
+        a.amp = at<float>(workspace, w.amp);
         a.need_pred = need_pred;
         a.mask_requested = mask_out != nullptr;
         a.events = h->profiling ? h->events : nullptr;
@@ -294,8 +305,11 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.need_pred = need_pred;
         a.mask_requested = mask_out != nullptr;
         a.events = h->profiling ? h->events : nullptr;
-        he = use_skinny(c, T) ? sffn::launch_skinny_forward(a, at<float>(workspace, w.partial), s)
-                              : sffn::launch_mfma_forward(a, s);
+        if (c.gate == SFFN_GATE_AMPLITUDE)
+            he = use_skinny(c, T) ? sffn::launch_amp_skinny(a, at<float>(workspace, w.partial), s)
+                                  : sffn::launch_amp_mfma(a, s);
+        else if (use_skinny(c, T)) he = sffn::launch_skinny_forward(a, at<float>(workspace, w.partial), s);
+        else he = sffn::launch_mfma_forward(a, s);
     }
     return hip_status(he, "sparse_ffn_forward");
 }
@@ -340,6 +354,13 @@ const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
     static const char* mfma[] = {"pred1_gemm", "pred2_gemm", "bank_topk", "gateup_gemm", "down_gemm"};
     static const char* mfma_fused[] = {"pred1_gemm", "pred2_topk_gemm", "none", "gateup_gemm", "down_gemm"};
     if (!h || i < 0 || i >= sffn::kStages) return nullptr;
+    if (h->cfg.gate == SFFN_GATE_AMPLITUDE) {
+        static const char* amp_gather[] = {"gateup_dense", "amp_topk", "down", "reduce", "none"};
+        static const char* amp_mfma[] = {"gateup_amp_gemm", "down_gemm", "none", "none", "none"};
+        static const char* amp_skinny[] = {"gateup_amp_gemm", "amp_topk", "down_gemm", "none", "none"};
+        if (use_gather(h->cfg, T)) return amp_gather[i];
+        return use_skinny(h->cfg, T) ? amp_skinny[i] : amp_mfma[i];
+    }
     // the dense fallback skips the predictor (and top-k) stages unless the
     // logits are asked for
     const bool dense_silu = h->cfg.gate == SFFN_GATE_SILU && h->cfg.keep == h->cfg.bank;

@@ -465,6 +465,44 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     reinterpret_cast<float4*>(out)[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
+// ---------------------------------------------------------------------------
+// Dense-4x baseline (post-hoc amplitude sparsity): one wave per (token,
+// bank) ranks |a| of the bank's 64 amplitudes a = SiLU(u) v, writes the mask
+// word, the kept channel ids in ascending order with their amplitudes (the h
+// of the down projection), and the amplitudes themselves when asked for.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_amp_topk(const float* __restrict__ amp, int64_t n_words, int nb,
+                                                  int keep, uint64_t* __restrict__ mask,
+                                                  float* __restrict__ out_amp, uint16_t* __restrict__ ids,
+                                                  float* __restrict__ hk, uint16_t* __restrict__ h_dense) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= n_words) return;
+    const int64_t t = w / nb;
+    const int b = (int)(w - t * nb);
+    const int d_i = nb * kBank;
+    const int j = b * kBank + lane;
+    const float v = amp[t * d_i + j];
+    const uint64_t sel = wave_bank_topk(rank_key(fabsf(v)), keep);
+    const bool kept = (sel >> lane) & 1ull;
+    if (lane == 0) mask[w] = sel;
+    if (out_amp) out_amp[t * d_i + j] = v;
+    if (h_dense) h_dense[t * d_i + j] = kept ? f32_to_bf16(v) : (uint16_t)0;
+    if (ids && kept) {
+        const int64_t slot = w * keep + lanes_below(sel);
+        ids[slot] = (uint16_t)j;
+        hk[slot] = v;
+    }
+}
+
+hipError_t launch_amp_mask(const float* amp, int64_t T, int d_i, int keep, uint64_t* mask, uint16_t* h_dense,
+                           hipStream_t s, void* const* events, int stage) {
+    const int nb = d_i / kBank;
+    xlaunch(events, stage, k_amp_topk, dim3((unsigned)((T * nb + 3) / 4)), dim3(256), 0, s, amp, T * nb, nb,
+            keep, mask, nullptr, nullptr, nullptr, h_dense);
+    return hipGetLastError();
+}
+
 int gather_groups(int d_s) { return (d_s + kGroup - 1) / kGroup; }
 
 bool fused_ok(const GatherArgs& a) {
@@ -479,6 +517,36 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
     const int64_t T = a.T;
     const int nch = a.d / 8;
     const int rb = a.dt == Dt::BF16 ? 1 : 0;
+    if (a.gate == kGateAmplitude) {
+        // Dense-4x baseline: dense gate/up (a = SiLU(u) v for every channel),
+        // the amplitude top-k, then down on the kept channels only
+        const int64_t n = T * a.d_i;
+        const dim3 grid((unsigned)((n + 3) / 4));
+        if (nch % (64 * NC) == 0)
+            xlaunch(a.events, 0, k_gateup<E, NC, true>, grid, dim3(256), 0, s, x,
+                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), nullptr, nullptr, a.amp,
+                    a.d, a.d_i, n, 1);
+        else
+            xlaunch(a.events, 0, k_gateup<E, NC, false>, grid, dim3(256), 0, s, x,
+                    static_cast<const E*>(a.W_g), static_cast<const E*>(a.W_u), nullptr, nullptr, a.amp,
+                    a.d, a.d_i, n, 1);
+        xlaunch(a.events, 1, k_amp_topk, dim3((unsigned)((T * nb + 3) / 4)), dim3(256), 0, s, a.amp,
+                T * nb, nb, a.keep, a.mask, a.logits, a.ids, a.h, nullptr);
+        const int groups = gather_groups(d_s);
+        const int slices = (a.d + kSlice - 1) / kSlice;
+        const dim3 dgrid((unsigned)(T * groups * slices));
+        if (a.d % kSlice == 0 && d_s % kGroup == 0)
+            xlaunch(a.events, 2, k_down<E, true>, dgrid, dim3(256), 0, s, static_cast<const E*>(a.W_dT),
+                    a.ids, a.h, a.partial, a.d, d_s, groups, slices);
+        else
+            xlaunch(a.events, 2, k_down<E, false>, dgrid, dim3(256), 0, s, static_cast<const E*>(a.W_dT),
+                    a.ids, a.h, a.partial, a.d, d_s, groups, slices);
+        const int col_blocks = (a.d + 31) / 32;
+        xlaunch(a.events, 3, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s, a.partial,
+                static_cast<E*>(a.y), a.d, groups, col_blocks);
+        skip_stages(a.events, 4, s);
+        return hipGetLastError();
+    }
     // every channel kept with the silu gate and no logits asked for: no
     // predictor and no top-k; gate/up and down walk all channels in order
     const bool dense = !a.need_pred;

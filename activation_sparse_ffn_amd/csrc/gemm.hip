@@ -20,7 +20,7 @@
 
 namespace sffn {
 
-enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_GATEUP = 2, EPI_PARTIAL = 3, EPI_TOPK = 4 };
+enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_GATEUP = 2, EPI_PARTIAL = 3, EPI_TOPK = 4, EPI_AMP = 5 };
 
 struct GemmParams {
     const uint16_t* A;   // [M, K]
@@ -363,7 +363,7 @@ constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab 
 template <int EPI, int WN>
 __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
     // WN waves along N (2 or 4), 2 along M: each wave owns 128 x (256 / WN) of C
-    constexpr bool GU = EPI == EPI_GATEUP;
+    constexpr bool GU = EPI == EPI_GATEUP || EPI == EPI_AMP;   // B = [W_g, W_u] blocks
     constexpr int NT = 128 * WN;                     // threads
     constexpr int WNC = TN / WN;                      // columns per wave
     constexpr int NJ = WNC / 32;                      // accumulator tiles along N
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     // gate/up with gate tiles: the 256 x 128 fp16 gate tile of an output block
     // is one contiguous 64 KB block
     auto gate_tile = [&](int mtile, int ntile) -> const uint16_t* {
-        if constexpr (GU)
+        if constexpr (EPI == EPI_GATEUP)
             if (p.G != nullptr)
                 return p.G + ((size_t)mtile * (p.N / kGateTileCols) + ntile) * (TM * kGateTileCols);
         return nullptr;
@@ -525,7 +525,63 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2)
     // + 4 (lane >> 5); for gate/up, tile j < NJ / 2 holds u and tile
     // j + NJ / 2 holds v of channels n0 + wn GB + 32 j + (lane & 31)
-    if constexpr (GU) {
+    if constexpr (EPI == EPI_AMP) {
+        // Dense-4x baseline: a = SiLU(u) v of the 256 x 128 block goes to LDS
+        // (both freed slab buffers) as 512 bank-rows q = 2 row + (col >> 6)
+        // of 256 bytes, 16-byte chunks swizzled by q; thread q then ranks
+        // |a| of its bank-row and writes the mask word, the masked bf16 h
+        // and, when asked for, the amplitudes
+        landed();
+        auto arow = [&](int q) { return (q < 256 ? buf0 : buf1) + (q & 255) * 256; };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+#pragma unroll
+                for (int j = 0; j < NJ / 2; ++j) {
+                    const int col = wn * GB + j * 32 + r32;
+                    const int q = 2 * rt + (col >> 6), c64 = col & 63;
+                    const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
+                    *reinterpret_cast<float*>(arow(q) + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
+                        sigmoidf_dev(u) * u * vv;
+                }
+            }
+        __syncthreads();
+        const int q = tid;                               // NT = 512 bank-rows
+        const int64_t t = m0 + (q >> 1);
+        const int j0 = n0 + (q & 1) * kBank;
+        const char* r = arow(q);
+        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(r + ((c ^ (q & 15)) << 4)); };
+        const uint64_t sel = lane_select64(
+            [&](int c) {
+                const float4 f = ld(c);
+                return make_float4(fabsf(f.x), fabsf(f.y), fabsf(f.z), fabsf(f.w));
+            },
+            p.keep);
+        if (t >= p.M || j0 >= p.N) return;
+        p.mask_w[t * (p.N / kBank) + j0 / kBank] = sel;
+        if (p.Cf != nullptr) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) reinterpret_cast<float4*>(p.Cf + t * p.N + j0)[c] = ld(c);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float4 v0 = ld(2 * c), v1 = ld(2 * c + 1);
+            const float av[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t hw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ch = 8 * c + 2 * e;
+                const uint32_t lo = ((sel >> ch) & 1ull) ? f32_to_bf16(av[2 * e]) : 0u;
+                const uint32_t hi = ((sel >> (ch + 1)) & 1ull) ? f32_to_bf16(av[2 * e + 1]) : 0u;
+                hw[e] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4*>(p.Cb + t * p.N + j0 + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+        return;
+    }
+    if constexpr (EPI == EPI_GATEUP) {
         if (gtile != nullptr || p.dense) {
             // H = select(kept, s u v, 0) with the gate values of the LDS
             // copy of the gate tile, written over them in place (each
@@ -598,7 +654,8 @@ template <int EPI>
 static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
     constexpr int WN = SFFN_GEMM256_WN;
     const int m_tiles = (int)((p.M + TM - 1) / TM);
-    const int n_tiles = (p.N + (EPI == EPI_GATEUP ? TN / 2 : TN) - 1) / (EPI == EPI_GATEUP ? TN / 2 : TN);
+    constexpr int TNC = (EPI == EPI_GATEUP || EPI == EPI_AMP) ? TN / 2 : TN;
+    const int n_tiles = (p.N + TNC - 1) / TNC;
     xlaunch(events, stage, k_gemm256<EPI, WN>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0, s, p,
             m_tiles, n_tiles);
 }
@@ -710,6 +767,19 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
     if (big) gemm256<EPI_BF16>(g, s, a.events, 4);
     else gemm<EPI_BF16>(g, s, a.events, 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_amp_mfma(const MfmaArgs& a, hipStream_t s) {
+    GemmParams g{};
+    g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;
+    g.mask_w = a.mask; g.keep = a.keep; g.Cf = a.logits_requested ? a.logits : nullptr;
+    gemm256<EPI_AMP>(g, s, a.events, 0);
+    g = GemmParams{};
+    g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
+    if (a.T >= 256) gemm256<EPI_BF16>(g, s, a.events, 1);
+    else gemm<EPI_BF16>(g, s, a.events, 1);
+    skip_stages(a.events, 2, s);
     return hipGetLastError();
 }
 

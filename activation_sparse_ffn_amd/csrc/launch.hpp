@@ -13,6 +13,9 @@ enum class Dt { F32 = 0, BF16 = 1 };
 
 constexpr int kStages = 5;
 
+// gate values (sffn_gate_t)
+constexpr int kGatePredictor = 0, kGateSilu = 1, kGateAmplitude = 2;
+
 // Launches one stage's kernel. With profiling events attached, events[2i]
 // and events[2i+1] take the start and end timestamps of this kernel's own
 // dispatch (hipExtLaunchKernel), so host launch gaps are not counted.
@@ -75,6 +78,7 @@ struct GatherArgs {
     float* pk;                      // [T, d_s]        kept logits
     float* h;                       // [T, d_s]        kept activations
     float* partial;                 // [T, groups, d]  down partial sums
+    float* amp;                     // [T, d_i] amplitudes (amplitude gate only)
     bool need_pred;                 // false: every channel kept with the silu gate
                                     // and no logits asked for, so no predictor
     bool mask_requested;            // mask points at the caller's mask_out
@@ -115,6 +119,15 @@ bool mfma_fused_topk(int64_t T, int d, int d_i, int rank);
 // bytes of the gate tiles for T tokens
 size_t gate_tiles_bytes(int64_t T, int d_i);
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s);
+// the Dense-4x baseline on the MFMA path: dense gate/up with the amplitude
+// top-k in its epilogue (mask, masked bf16 h, amplitudes into logits when
+// asked for), then the down GEMM
+hipError_t launch_amp_mfma(const MfmaArgs& a, hipStream_t s);
+// the same for 4 < T <= 64 on the skinny kernels (amplitudes through logits)
+hipError_t launch_amp_skinny(const MfmaArgs& a, float* partial, hipStream_t s);
+// bank top-k of |amp| [T, d_i]: mask words and the masked bf16 h [T, d_i]
+hipError_t launch_amp_mask(const float* amp, int64_t T, int d_i, int keep, uint64_t* mask, uint16_t* h_dense,
+                           hipStream_t s, void* const* events, int stage);
 
 // ---- skinny MFMA path (bf16, 4 < T <= 64, rank % 64 == 0) -----------------
 size_t skinny_partial_floats(int64_t T, int d, int rank, int d_i);

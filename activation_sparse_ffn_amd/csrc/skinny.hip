@@ -25,7 +25,7 @@
 
 namespace sffn {
 
-enum { SK_BF16 = 0, SK_F32_BIAS = 1, SK_GATEUP = 2, SK_PARTIAL = 3 };
+enum { SK_BF16 = 0, SK_F32_BIAS = 1, SK_GATEUP = 2, SK_PARTIAL = 3, SK_AMP = 4 };
 
 struct SkinnyParams {
     const uint16_t* A;     // [M, K]
@@ -192,6 +192,10 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
                 p.Cb[o] = f32_to_bf16(val[0]);
             } else if constexpr (EPI == SK_F32_BIAS) {
                 p.Cf[o] = val[0] + (p.bias ? p.bias[n] : 0.f);
+            } else if constexpr (EPI == SK_AMP) {
+                // Dense-4x baseline: the amplitude SiLU(u) v of every channel, fp32
+                const float u = val[0], vv = val[NB - 1];
+                p.Cf[o] = sigmoidf_dev(u) * u * vv;
             } else {
                 const float u = val[0], vv = val[NB - 1];
                 const bool keep = (p.mask[(size_t)m * (p.N / kBank) + (n >> 6)] >> (n & 63)) & 1ull;
@@ -298,6 +302,31 @@ hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t 
             sum_bf16(partial, a.y, sp, (int64_t)M * a.d, s, a.events, 4);
         }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_amp_skinny(const MfmaArgs& a, float* partial, hipStream_t s) {
+    const int M = (int)a.T;
+    // amplitudes of every channel (fp32, into logits)
+    SkinnyParams p{};
+    p.A = a.x; p.B0 = a.W_g; p.B1 = a.W_u; p.M = M; p.N = a.d_i; p.K = a.d; p.Cf = a.logits;
+    skinny<SK_AMP, 2>(p, 1, s, a.events, 0, true);
+    // bank top-k of |a|: the mask and the masked bf16 h
+    hipError_t e = launch_amp_mask(a.logits, a.T, a.d_i, a.keep, a.mask, a.h, s, a.events, 1);
+    if (e != hipSuccess) return e;
+    // Y = bf16(H W_d^T)
+    const int sp = k_splits(a.d, a.d_i);
+    p = SkinnyParams{};
+    p.A = a.h; p.B0 = a.W_d; p.M = M; p.N = a.d; p.K = a.d_i;
+    if (sp == 1) {
+        p.Cb = a.y;
+        skinny<SK_BF16, 1>(p, 1, s, a.events, 2, true);
+    } else {
+        p.partial = partial;
+        skinny<SK_PARTIAL, 1>(p, sp, s, a.events, 2, false);
+        sum_bf16(partial, a.y, sp, (int64_t)M * a.d, s, a.events, 2);
+    }
+    skip_stages(a.events, 3, s);
     return hipGetLastError();
 }
 

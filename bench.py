@@ -62,8 +62,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--keep", type=int, default=16,
                     help="channels kept per 64-channel bank (64: the dense modes)")
-    ap.add_argument("--gate", choices=["pred", "silu"], default="pred",
-                    help="gate of the kept channels: sigmoid of the predictor logit or of u")
+    ap.add_argument("--gate", choices=["pred", "silu", "amplitude"], default="pred",
+                    help="gate of the kept channels: sigmoid of the predictor logit or of u; "
+                         "amplitude: the Dense-4x post-hoc baseline (no predictor)")
     return ap.parse_args()
 
 
@@ -80,6 +81,19 @@ def algorithmic(wl_name, shape, T, masks_union_frac=None, gate="pred"):
     """
     d, d_i, r, ds = shape.d, shape.d_i, shape.rank, shape.d_s
     e = 2
+    if gate == "amplitude":
+        # Dense-4x baseline: gate and up for every channel, down on kept ones
+        row = d * e
+        gateup = 2 * d_i * row
+        if wl_name == "decode":
+            gateup, down = gateup * T, ds * row * T
+        else:
+            down = int(masks_union_frac * d_i * row)
+        out = dict(pred=0, gateup=gateup, down=down, bytes=gateup + down,
+                   flops=2 * T * (2 * d_i * d + ds * d))
+        if wl_name != "decode":
+            out["executed_flops"] = 2 * T * 3 * d_i * d
+        return out
     no_pred = gate == "silu" and shape.keep == shape.bank
     pred = 0 if no_pred else (r * d + d_i * r) * e
     if no_pred:
@@ -355,7 +369,8 @@ def main():
             dom, kname = "bank_fused", "k_bank_fused"
             nbytes = alg["pred_b"] + alg["gateup"] + alg["down"]
         else:
-            dom, kname = "gateup", "k_gateup"
+            dom = next(n for n in names if n.startswith("gateup"))
+            kname = "k_gateup"
             nbytes = alg["gateup"]
         dur_s = stage_us[names.index(dom)] * 1e-6
         achieved = nbytes / dur_s / 1e9
@@ -363,7 +378,7 @@ def main():
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=profiled_traffic(kname),
                     bytes_per_launch=nbytes, avg_us=round(float(stage_us[names.index(dom)]), 3))
     else:
-        dom = "gateup_gemm"
+        dom = next(n for n in names if n.startswith("gateup"))
         dur_s = stage_us[names.index(dom)] * 1e-6
         fl = 2 * T * 2 * shape.d_i * shape.d        # executed: dense gate and up
         achieved = fl / dur_s / 1e12

@@ -64,7 +64,14 @@ typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype_t;
 
 typedef enum {
     SFFN_GATE_PREDICTOR = 0,   /* h = m * sigmoid(p) * u * v                */
-    SFFN_GATE_SILU = 1         /* h = m * sigmoid(u) * u * v                */
+    SFFN_GATE_SILU = 1,        /* h = m * sigmoid(u) * u * v                */
+    /* The Dense-4x baseline the method is compared against ("Continual LLM
+     * Upcycling", gist.science technical summary, Resultaten: naive 4x
+     * sparsity applied post hoc from activation amplitude). No predictor:
+     * gate and up run for every channel, m is the bank top-k of
+     * |sigmoid(u) * u * v| (fp32), h = m * sigmoid(u) * u * v, and down
+     * reads the kept channels only. */
+    SFFN_GATE_AMPLITUDE = 2
 } sffn_gate_t;
 
 /* Layer shape. The method's layer is d_i = 14336, rank = 448, bank = 64,
@@ -93,6 +100,7 @@ size_t sparse_ffn_packed_size(const sffn_config_t* cfg);
  *   pred_a  [rank, d]  predictor layer 1               (device, cfg->dtype)
  *   pred_b  [d_i, rank] predictor layer 2              (device, cfg->dtype)
  *   pred_bias [d_i] fp32 or NULL                       (device)
+ * With SFFN_GATE_AMPLITUDE pred_a and pred_b may be NULL (unused).
  * The weights may be freed after this call returns; `packed` must stay alive
  * and unmodified until sparse_ffn_destroy. Synchronises `hip_stream`.
  * *out is set only on SFFN_OK. */
@@ -109,7 +117,9 @@ size_t sparse_ffn_workspace_size(sffn_handle_t h, int64_t T);
 
 /* Forward of T tokens: x [T, d] -> y [T, d] (device, cfg->dtype).
  *   mask_out   [T, d_i/64] uint64 or NULL: the top-k mask actually used
- *   logits_out [T, d_i] fp32 or NULL: the predictor logits p
+ *   logits_out [T, d_i] fp32 or NULL: the predictor logits p (with
+ *              SFFN_GATE_AMPLITUDE: the amplitudes sigmoid(u) * u * v that
+ *              were ranked)
  *   workspace  device scratch of >= sparse_ffn_workspace_size(h, T) bytes,
  *              not shared with a concurrent call
  * keep = 64 keeps every channel: with SFFN_GATE_PREDICTOR it is the
