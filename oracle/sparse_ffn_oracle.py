@@ -37,6 +37,18 @@ Readings where the pages are silent (each one is listed in the design doc):
   h_j = m_j * sigma(u_j) * u_j * v_j ("silu");
 * y is returned in float64; callers compare the GPU's y after widening.
 
+The backward pass follows the same summary's Executie > Backward Pass: the
+non-differentiable top-k is crossed by a soft, sigmoid-like local gradient
+around the selection threshold, so the language-modelling loss reaches the
+predictor. Its form is not given; the reading taken here (listed in
+the design doc): the forward keeps the hard mask m; the backward differentiates
+m as if it were sigmoid((p - theta) / tau), with theta the midpoint of the
+bank's keep-th and (keep+1)-th largest logits (held constant) and tau > 0 the
+caller's temperature; the mask's gradient g_h * s * u * v is taken for every
+channel (so gate and up are evaluated densely, as the authors' GPU runs do);
+the bf16 rounding of z passes gradients unchanged; with keep == bank there
+is no threshold and no surrogate term.
+
 It also computes the Dense-4x baseline the pages compare against (same
 summary, Resultaten: naive 4x sparsity applied post hoc from activation
 amplitude): gate and up run dense, the per-bank top-k ranks the amplitude
@@ -55,7 +67,7 @@ import numpy as np
 __all__ = [
     "widen", "round_to_bf16", "bf16_bits_of", "sigmoid", "predictor_logits",
     "bank_topk_mask", "mask_to_words", "words_to_mask", "sparse_swiglu",
-    "forward", "logit_gap", "amplitude_forward",
+    "forward", "logit_gap", "amplitude_forward", "bank_threshold", "backward",
 ]
 
 
@@ -308,3 +320,81 @@ def amplitude_forward(x, W_g, W_u, W_d, bank: int = 64, keep: int = 16,
         S = np.flatnonzero(m[n])
         y[n] = widen(Wd[:, S]) @ a[n, S]
     return dict(a=a, score=score, mask=m, words=mask_to_words(m, bank), h=h, y=y, tokens=rows)
+
+
+# ----------------------------------------------------------------------------
+# backward pass (Executie > Backward Pass: soft surrogate gradient around the
+# bank threshold; the form is the reading stated in the module docstring)
+# ----------------------------------------------------------------------------
+
+def bank_threshold(p: np.ndarray, bank: int = 64, keep: int = 16) -> np.ndarray:
+    """Per (token, bank): the midpoint of the keep-th and (keep+1)-th largest
+    logits, NaN counted below every number (NaN when keep == bank)."""
+    T, d_i = p.shape
+    v = np.asarray(p, dtype=np.float64).reshape(T, d_i // bank, bank)
+    v = np.where(np.isnan(v), -np.inf, v)
+    v = -np.sort(-v, axis=-1)
+    if keep >= bank:
+        return np.full(v.shape[:2], np.nan)
+    return 0.5 * (v[..., keep - 1] + v[..., keep])
+
+
+def _dsigmoid(a: np.ndarray) -> np.ndarray:
+    s = sigmoid(a)
+    return s * (1.0 - s)
+
+
+def backward(x, A, B, W_g, W_u, W_d, g_y, bias=None, bank: int = 64, keep: int = 16,
+             gate: str = "pred", tau: float = 1.0,
+             round_z_bf16: Optional[bool] = None) -> dict:
+    """Gradients of L = sum(y * g_y) for every input of the layer.
+
+    Returns g_x [T, d], g_A [rank, d], g_B [d_i, rank], g_bias [d_i] (or
+    None), g_Wg, g_Wu [d_i, d], g_Wd [d, d_i], and the intermediates g_h,
+    g_p, theta and the mask, all float64. ``tau = inf`` switches the
+    surrogate term off (the derivative of the hard-mask forward).
+    """
+    if gate not in ("pred", "silu"):
+        raise ValueError("gate must be 'pred' or 'silu'")
+    x = np.asarray(x)
+    if round_z_bf16 is None:
+        round_z_bf16 = x.dtype == np.uint16
+    X = widen(x)
+    Aw, Bw, Wg, Wu, Wd = widen(A), widen(B), widen(W_g), widen(W_u), widen(W_d)
+    G = widen(g_y)
+    # forward, as the forward pass computes it
+    z, p32 = predictor_logits(x, A, B, bias, round_z_bf16)
+    m = bank_topk_mask(p32, bank, keep).astype(np.float64)
+    p = p32.astype(np.float64)
+    U = X @ Wg.T
+    V = X @ Wu.T
+    s = sigmoid(p) if gate == "pred" else sigmoid(U)
+    h = m * s * U * V
+    # down
+    g_h = G @ Wd                       # dL/dh for every channel
+    g_Wd = G.T @ h
+    # through h = m * s * u * v
+    if gate == "pred":
+        g_U = m * g_h * s * V
+        g_p = m * g_h * U * V * _dsigmoid(p)
+    else:
+        g_U = m * g_h * V * (s + U * _dsigmoid(U))
+        g_p = np.zeros_like(p)
+    g_V = m * g_h * s * U
+    # the surrogate gradient of the mask
+    T, d_i = p.shape
+    theta = bank_threshold(p, bank, keep)
+    if keep < bank and np.isfinite(tau):
+        th = np.repeat(theta, bank, axis=1)
+        g_m = g_h * s * U * V
+        g_p = g_p + g_m * _dsigmoid((p - th) / tau) / tau
+    # the predictor (z's bf16 rounding passes gradients unchanged)
+    g_bias = g_p.sum(axis=0) if bias is not None else None
+    g_B = g_p.T @ z
+    g_z = g_p @ Bw
+    g_A = g_z.T @ X
+    g_x = g_z @ Aw + g_U @ Wg + g_V @ Wu
+    g_Wg = g_U.T @ X
+    g_Wu = g_V.T @ X
+    return dict(g_x=g_x, g_A=g_A, g_B=g_B, g_bias=g_bias, g_Wg=g_Wg, g_Wu=g_Wu, g_Wd=g_Wd,
+                g_h=g_h, g_p=g_p, theta=theta, mask=m.astype(bool), z=z, p=p)
