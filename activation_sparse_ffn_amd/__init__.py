@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "sparse_ffn_packed_size", "sparse_ffn_create", "sparse_ffn_workspace_size",
     "sparse_ffn_forward", "bank_topk", "sparse_ffn_destroy", "sparse_ffn_status_string",
     "sparse_ffn_last_error", "sparse_ffn_set_stage_events", "sparse_ffn_stage_name",
+    "sparse_ffn_backward_workspace_size", "sparse_ffn_backward",
 )
 SFFN_STAGES = 5
 
@@ -92,6 +93,10 @@ def load_library():
     lib.sparse_ffn_set_stage_events.restype = st
     lib.sparse_ffn_stage_name.argtypes = [P, I64, I32]
     lib.sparse_ffn_stage_name.restype = ctypes.c_char_p
+    lib.sparse_ffn_backward_workspace_size.argtypes = [P, I64]
+    lib.sparse_ffn_backward_workspace_size.restype = S
+    lib.sparse_ffn_backward.argtypes = [P, P, P, P, I64, ctypes.c_float, P, P, P, P, P, P, P, P, S, P]
+    lib.sparse_ffn_backward.restype = st
     _LIB = lib
     return lib
 
@@ -186,6 +191,7 @@ class SparseFFN:
             _ptr(self.packed), size, _stream(self.device), ctypes.byref(h)))
         self._h = h
         self._ws = None
+        self.has_bias = bias is not None
 
     @property
     def d(self):
@@ -231,6 +237,35 @@ class SparseFFN:
         return out[0] if len(out) == 1 else tuple(out)
 
     __call__ = forward
+
+    def backward(self, x: torch.Tensor, g_y: torch.Tensor, mask: torch.Tensor, tau: float = 1.0,
+                 workspace: Optional[torch.Tensor] = None) -> dict:
+        """Gradients of sum(y * g_y) for a forward of x that returned `mask`
+        (bf16 layers; predictor or silu gate). The top-k's derivative is the
+        soft surrogate sigmoid((p - theta) / tau) around each bank's
+        threshold; tau = float("inf") leaves it out. Returns fp32 tensors
+        "x", "A", "B", "bias" (None without a bias), "W_g", "W_u", "W_d"."""
+        _need_gpu(x, g_y, mask)
+        if x.dtype != self.dtype or g_y.dtype != self.dtype or x.shape != g_y.shape or x.dim() != 2 \
+                or x.shape[1] != self.d:
+            raise ValueError(f"x and g_y must be [T, {self.d}] {self.dtype}")
+        T = x.shape[0]
+        if mask.shape != (T, self.d_i // 64) or mask.dtype != torch.int64:
+            raise ValueError("mask must be the forward's [T, d_i / 64] int64 mask")
+        f32 = dict(dtype=torch.float32, device=self.device)
+        r = self.cfg.rank
+        out = {"x": torch.empty((T, self.d), **f32), "A": torch.empty((r, self.d), **f32),
+               "B": torch.empty((self.d_i, r), **f32), "W_g": torch.empty((self.d_i, self.d), **f32),
+               "W_u": torch.empty((self.d_i, self.d), **f32), "W_d": torch.empty((self.d, self.d_i), **f32),
+               "bias": torch.empty(self.d_i, **f32) if self.has_bias else None}
+        need = int(self._lib.sparse_ffn_backward_workspace_size(self._h, T))
+        ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8,
+                                                                   device=self.device)
+        _check(self._lib, self._lib.sparse_ffn_backward(
+            self._h, _ptr(x), _ptr(g_y), _ptr(mask), T, ctypes.c_float(tau), _ptr(out["x"]), _ptr(out["A"]),
+            _ptr(out["B"]), _ptr(out["bias"]), _ptr(out["W_g"]), _ptr(out["W_u"]), _ptr(out["W_d"]),
+            _ptr(ws), ws.numel(), _stream(self.device)))
+        return out
 
     def set_stage_events(self, events):
         """Attach 2 * SFFN_STAGES raw hipEvent_t handles (ints): the start and

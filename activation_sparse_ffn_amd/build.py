@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_ffn.so")
-SOURCES = ["topk.hip", "gather.hip", "gemm.hip", "skinny.hip", "capi.cpp"]
+SOURCES = ["topk.hip", "gather.hip", "gemm.hip", "skinny.hip", "backward.hip", "capi.cpp"]
 ARCH = os.environ.get("SFFN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

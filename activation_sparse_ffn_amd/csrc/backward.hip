@@ -1,0 +1,233 @@
+// Backward pass of the predictor-gated sparse SwiGLU FFN ("Continual LLM
+// Upcycling", gist.science technical summary, Methodologie > 1. Architectuur,
+// Executie > Backward Pass): the hard top-k is crossed by a soft,
+// sigmoid-like local gradient around the bank's selection threshold, so the
+// loss reaches the predictor.
+//
+// Reading of the unstated form: the forward's hard mask m is differentiated
+// as sigmoid((p - theta) / tau), theta the midpoint of the bank's smallest
+// kept and largest dropped logit (its keep-th and (keep+1)-th largest; NaN
+// counts lowest) held constant, tau the caller's temperature (1/tau = 0: no
+// surrogate term). The mask gradient g_h * s * u * v is taken for every
+// channel, so gate and up are evaluated densely. z's bf16 rounding passes
+// gradients unchanged. A full bank (keep = 64) has no threshold.
+//
+// Steps, for T tokens (bf16 operands, fp32 accumulation, fp32 gradients):
+//   z = bf16(x A^T), p = z B^T + bias          recomputed forward logits
+//   g_h = g_y W_d                               every channel (W_d^T packed)
+//   U = x W_g^T, V = x W_u^T                    dense, fp32
+//   k_bwd_bank: theta, h, g_u, g_v, g_p         one wave per (token, bank)
+//   g_W_d = g_y^T h, g_W_g = g_u^T x, g_W_u = g_v^T x, g_B = g_p^T z,
+//   g_z = g_p B, g_A = g_z^T x, g_bias = sum_t g_p,
+//   g_x = g_z A + g_u W_g + g_v W_u
+// Every product runs as C = A B^T on the MFMA GEMMs; operands that the
+// tokens must contract over are transposed first, zero-padded to a multiple
+// of 64 tokens.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sffn {
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// One wave per (token, bank), one channel per lane.
+__global__ __launch_bounds__(256) void k_bwd_bank(const float* __restrict__ p, const float* __restrict__ U,
+                                                  const float* __restrict__ V, const float* __restrict__ g_h,
+                                                  const uint64_t* __restrict__ mask, int64_t n_words, int nb,
+                                                  int gate, int keep, float inv_tau,
+                                                  uint16_t* __restrict__ h_out, uint16_t* __restrict__ g_u,
+                                                  uint16_t* __restrict__ g_v, float* __restrict__ g_p32,
+                                                  uint16_t* __restrict__ g_p16) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= n_words) return;
+    const int64_t t = w / nb;
+    const int b = (int)(w - t * nb);
+    const int64_t o = t * (int64_t)nb * kBank + b * kBank + lane;
+    const float pv = p[o], u = U[o], v = V[o], gh = g_h[o];
+    const bool kept = (mask[w] >> lane) & 1ull;
+    const float m = kept ? 1.f : 0.f;
+    // threshold: midpoint of the smallest kept and the largest dropped logit
+    const float key = __builtin_isnan(pv) ? -__builtin_huge_valf() : pv;
+    const float kmin = wave_min(kept ? key : __builtin_huge_valf());
+    const float dmax = wave_max(kept ? -__builtin_huge_valf() : key);
+    const float sp = sigmoidf_dev(pv), su = sigmoidf_dev(u);
+    const float s = gate ? su : sp;
+    const float gm = gh * s * u * v;                 // dL/dm
+    const float gu = gate ? m * gh * v * (su + u * su * (1.f - su)) : m * gh * s * v;
+    const float gv = m * gh * s * u;
+    float gp = gate ? 0.f : m * gh * u * v * sp * (1.f - sp);
+    if (keep < kBank && inv_tau > 0.f) {
+        const float theta = 0.5f * (kmin + dmax);
+        const float sa = sigmoidf_dev((pv - theta) * inv_tau);
+        gp += gm * sa * (1.f - sa) * inv_tau;
+    }
+    h_out[o] = f32_to_bf16(m * s * u * v);
+    g_u[o] = f32_to_bf16(gu);
+    g_v[o] = f32_to_bf16(gv);
+    g_p32[o] = gp;
+    g_p16[o] = f32_to_bf16(gp);
+}
+
+// out[c] = sum over rows of x[r][c] in a fixed order: thread (column,
+// eighth) sums every eighth row in order, then the eighths are summed in order
+__global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ x, int64_t rows, int cols,
+                                                float* __restrict__ out) {
+    __shared__ float red[8][32];
+    const int cl = threadIdx.x & 31, q = threadIdx.x >> 5;
+    const int c = blockIdx.x * 32 + cl;
+    float a = 0.f;
+    if (c < cols)
+        for (int64_t r = q; r < rows; r += 8) a += x[r * cols + c];
+    red[q][cl] = a;
+    __syncthreads();
+    if (q == 0 && c < cols) {
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum += red[k][cl];
+        out[c] = sum;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ x, int64_t n, float v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) x[i] = v;
+}
+
+namespace {
+constexpr size_t kWsAlign = 256;
+size_t up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct BwdLayout {
+    size_t z16, p32, gh32, U32, V32, h16, gu16, gv16, gp32, gp16, gz16;
+    size_t GT, hT, XT, guT, gvT, gpT, zT, gzT, BT, AT, WgT, WuT, total;
+};
+
+BwdLayout layout(int64_t T, int d, int d_i, int r) {
+    const size_t Tp = (size_t)((T + 63) / 64 * 64);
+    const size_t tdi = (size_t)T * d_i;
+    BwdLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
+    L.z16 = take((size_t)T * r * 2);
+    L.p32 = take(tdi * 4);
+    L.gh32 = take(tdi * 4);
+    L.U32 = take(tdi * 4);
+    L.V32 = take(tdi * 4);
+    L.h16 = take(tdi * 2);
+    L.gu16 = take(tdi * 2);
+    L.gv16 = take(tdi * 2);
+    L.gp32 = take(tdi * 4);
+    L.gp16 = take(tdi * 2);
+    L.gz16 = take((size_t)T * r * 2);
+    L.GT = take((size_t)d * Tp * 2);
+    L.hT = take((size_t)d_i * Tp * 2);
+    L.XT = take((size_t)d * Tp * 2);
+    L.guT = take((size_t)d_i * Tp * 2);
+    L.gvT = take((size_t)d_i * Tp * 2);
+    L.gpT = take((size_t)d_i * Tp * 2);
+    L.zT = take((size_t)r * Tp * 2);
+    L.gzT = take((size_t)r * Tp * 2);
+    L.BT = take((size_t)r * d_i * 2);
+    L.AT = take((size_t)d * r * 2);
+    L.WgT = take((size_t)d * d_i * 2);
+    L.WuT = take((size_t)d * d_i * 2);
+    L.total = off;
+    return L;
+}
+
+template <typename P>
+P* at(void* base, size_t off) {
+    return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t T, int d, int d_i, int rank) { return layout(T, d, d_i, rank).total; }
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+    const int64_t T = a.T;
+    const int d = a.d, d_i = a.d_i, r = a.rank, nb = d_i / kBank;
+    const int Tp = (int)((T + 63) / 64 * 64);
+    const BwdLayout L = layout(T, d, d_i, r);
+    void* ws = a.ws;
+    uint16_t* z16 = at<uint16_t>(ws, L.z16);
+    float* p32 = at<float>(ws, L.p32);
+    float* gh32 = at<float>(ws, L.gh32);
+    float* U32 = at<float>(ws, L.U32);
+    float* V32 = at<float>(ws, L.V32);
+    uint16_t* h16 = at<uint16_t>(ws, L.h16);
+    uint16_t* gu16 = at<uint16_t>(ws, L.gu16);
+    uint16_t* gv16 = at<uint16_t>(ws, L.gv16);
+    float* gp32 = at<float>(ws, L.gp32);
+    uint16_t* gp16 = at<uint16_t>(ws, L.gp16);
+    uint16_t* gz16 = at<uint16_t>(ws, L.gz16);
+    uint16_t* GT = at<uint16_t>(ws, L.GT);
+    uint16_t* hT = at<uint16_t>(ws, L.hT);
+    uint16_t* XT = at<uint16_t>(ws, L.XT);
+    uint16_t* guT = at<uint16_t>(ws, L.guT);
+    uint16_t* gvT = at<uint16_t>(ws, L.gvT);
+    uint16_t* gpT = at<uint16_t>(ws, L.gpT);
+    uint16_t* zT = at<uint16_t>(ws, L.zT);
+    uint16_t* gzT = at<uint16_t>(ws, L.gzT);
+    uint16_t* BT = at<uint16_t>(ws, L.BT);
+    uint16_t* AT = at<uint16_t>(ws, L.AT);
+    uint16_t* WgT = at<uint16_t>(ws, L.WgT);
+    uint16_t* WuT = at<uint16_t>(ws, L.WuT);
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; return e == hipSuccess; };
+
+    // recomputed forward: z, p, dense U and V; g_h for every channel
+    ok(launch_gemm_nt(a.x, a.A, T, r, d, z16, GemmOut::BF16, s));
+    ok(launch_gemm_nt(z16, a.B, T, d_i, r, p32, GemmOut::F32, s, a.bias));
+    ok(launch_gemm_nt(a.g_y, a.W_dT, T, d_i, d, gh32, GemmOut::F32, s));
+    ok(launch_uv_gemm(a.x, a.W_g, a.W_u, T, d_i, d, U32, V32, s));
+    hipLaunchKernelGGL(k_bwd_bank, dim3((unsigned)((T * nb + 3) / 4)), dim3(256), 0, s, p32, U32, V32, gh32,
+                       a.mask, T * nb, nb, a.gate, a.keep, a.inv_tau, h16, gu16, gv16, gp32, gp16);
+    ok(hipGetLastError());
+    if (a.g_bias) {
+        hipLaunchKernelGGL(k_colsum, dim3((unsigned)((d_i + 31) / 32)), dim3(256), 0, s, gp32, T, d_i, a.g_bias);
+        ok(hipGetLastError());
+    }
+    // token-major operands transposed for the weight gradients (K = tokens)
+    ok(launch_transpose(Dt::BF16, a.g_y, GT, (int)T, d, s, Tp));
+    ok(launch_transpose(Dt::BF16, h16, hT, (int)T, d_i, s, Tp));
+    ok(launch_transpose(Dt::BF16, a.x, XT, (int)T, d, s, Tp));
+    ok(launch_transpose(Dt::BF16, gu16, guT, (int)T, d_i, s, Tp));
+    ok(launch_transpose(Dt::BF16, gv16, gvT, (int)T, d_i, s, Tp));
+    ok(launch_transpose(Dt::BF16, gp16, gpT, (int)T, d_i, s, Tp));
+    ok(launch_transpose(Dt::BF16, z16, zT, (int)T, r, s, Tp));
+    ok(launch_gemm_nt(GT, hT, d, d_i, Tp, a.g_Wd, GemmOut::F32, s));
+    ok(launch_gemm_nt(guT, XT, d_i, d, Tp, a.g_Wg, GemmOut::F32, s));
+    ok(launch_gemm_nt(gvT, XT, d_i, d, Tp, a.g_Wu, GemmOut::F32, s));
+    ok(launch_gemm_nt(gpT, zT, d_i, r, Tp, a.g_B, GemmOut::F32, s));
+    // the predictor's input side
+    ok(launch_transpose(Dt::BF16, a.B, BT, d_i, r, s));
+    ok(launch_gemm_nt(gp16, BT, T, r, d_i, gz16, GemmOut::BF16, s));
+    ok(launch_transpose(Dt::BF16, gz16, gzT, (int)T, r, s, Tp));
+    ok(launch_gemm_nt(gzT, XT, r, d, Tp, a.g_A, GemmOut::F32, s));
+    // g_x = g_z A + g_u W_g + g_v W_u
+    ok(launch_transpose(Dt::BF16, a.A, AT, r, d, s));
+    ok(launch_transpose(Dt::BF16, a.W_g, WgT, d_i, d, s));
+    ok(launch_transpose(Dt::BF16, a.W_u, WuT, d_i, d, s));
+    ok(launch_gemm_nt(gz16, AT, T, d, r, a.g_x, GemmOut::F32, s));
+    ok(launch_gemm_nt(gu16, WgT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s));
+    ok(launch_gemm_nt(gv16, WuT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s));
+    return e;
+}
+
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s) {
+    if (x == nullptr || n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, n, 0.f);
+    return hipGetLastError();
+}
+
+}  // namespace sffn

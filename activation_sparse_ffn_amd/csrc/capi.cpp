@@ -11,6 +11,7 @@
 //                      the matrix cores
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
@@ -312,6 +313,74 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         else he = sffn::launch_mfma_forward(a, s);
     }
     return hip_status(he, "sparse_ffn_forward");
+}
+
+size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T) {
+    if (!h || T <= 0) return 0;
+    return sffn::backward_workspace_bytes(T, h->cfg.d, h->cfg.d_i, h->cfg.rank);
+}
+
+sffn_status_t sparse_ffn_backward(sffn_handle_t h, const void* x, const void* g_y, const uint64_t* mask,
+                                  int64_t T, float tau, float* g_x, float* g_A, float* g_B, float* g_bias,
+                                  float* g_Wg, float* g_Wu, float* g_Wd, void* workspace, size_t ws_bytes,
+                                  void* hip_stream) {
+    if (!h) return fail(SFFN_ERR_INVALID_ARG, "handle is null");
+    const sffn_config_t& c = h->cfg;
+    if (c.dtype != SFFN_BF16) return fail(SFFN_ERR_UNSUPPORTED, "the backward pass needs a bf16 layer");
+    if (c.gate == SFFN_GATE_AMPLITUDE)
+        return fail(SFFN_ERR_UNSUPPORTED, "the backward pass has no amplitude-gate form");
+    if (T < 0) return fail(SFFN_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (!(tau > 0.f)) return fail(SFFN_ERR_INVALID_ARG, "tau must be > 0 (got %g)", (double)tau);
+    float* outs[] = {g_x, g_A, g_B, g_Wg, g_Wu, g_Wd};
+    const char* names[] = {"g_x", "g_A", "g_B", "g_Wg", "g_Wu", "g_Wd"};
+    for (int i = 0; i < 6; ++i) {
+        if (!outs[i]) {
+            if (i == 0 && T == 0) continue;          // g_x has no elements then
+            return fail(SFFN_ERR_INVALID_ARG, "%s is null", names[i]);
+        }
+        if (!aligned16(outs[i])) return fail(SFFN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (g_bias && !aligned16(g_bias)) return fail(SFFN_ERR_INVALID_ARG, "g_bias is not 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int64_t d = c.d, di = c.d_i, r = c.rank;
+    if (T == 0) {
+        hipError_t he = hipSuccess;
+        const struct { float* p; int64_t n; } z[] = {{g_A, r * d}, {g_B, di * r}, {g_bias, di},
+                                                      {g_Wg, di * d}, {g_Wu, di * d}, {g_Wd, d * di}};
+        for (const auto& q : z)
+            if (he == hipSuccess) he = sffn::launch_zero_f32(q.p, q.n, s);
+        return hip_status(he, "sparse_ffn_backward");
+    }
+    if (!x || !g_y || !mask) return fail(SFFN_ERR_INVALID_ARG, "x, g_y and mask must not be null");
+    if (!aligned16(x) || !aligned16(g_y) || !aligned16(mask))
+        return fail(SFFN_ERR_INVALID_ARG, "x, g_y and mask must be 16-byte aligned");
+    if (!workspace) return fail(SFFN_ERR_INVALID_ARG, "workspace is null");
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+        return fail(SFFN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (T * di / 4 >= kMaxGrid || T > (int64_t)1 << 24)
+        return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
+    const size_t need = sparse_ffn_backward_workspace_size(h, T);
+    if (ws_bytes < need)
+        return fail(SFFN_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed for T = %lld", ws_bytes, need,
+                    (long long)T);
+    const PackedLayout& L = h->L;
+    void* pk = h->packed;
+    sffn::BwdArgs a{};
+    a.d = c.d; a.d_i = c.d_i; a.rank = c.rank; a.keep = c.keep; a.gate = (int)c.gate; a.T = T;
+    a.inv_tau = std::isinf(tau) ? 0.f : 1.f / tau;
+    a.x = static_cast<const uint16_t*>(x);
+    a.g_y = static_cast<const uint16_t*>(g_y);
+    a.mask = mask;
+    a.A = at<const uint16_t>(pk, L.A); a.B = at<const uint16_t>(pk, L.B);
+    a.bias = h->has_bias ? at<const float>(pk, L.bias) : nullptr;
+    a.W_g = at<const uint16_t>(pk, L.Wg); a.W_u = at<const uint16_t>(pk, L.Wu);
+    a.W_dT = at<const uint16_t>(pk, L.WdT);
+    a.g_x = g_x; a.g_A = g_A; a.g_B = g_B; a.g_Wg = g_Wg; a.g_Wu = g_Wu; a.g_Wd = g_Wd;
+    a.g_bias = h->has_bias ? g_bias : nullptr;
+    a.ws = workspace;
+    hipError_t he = sffn::launch_backward(a, s);
+    if (he == hipSuccess && g_bias && !h->has_bias) he = sffn::launch_zero_f32(g_bias, di, s);
+    return hip_status(he, "sparse_ffn_backward");
 }
 
 sffn_status_t bank_topk(const float* logits, int64_t T, int32_t d_i, int32_t keep,

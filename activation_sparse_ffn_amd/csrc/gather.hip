@@ -620,31 +620,34 @@ hipError_t launch_gather_forward(const GatherArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // packing: out-of-place transpose through LDS, 64 x 64 tiles
 // ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c] with dst rows of ld >= rows entries; entries
+// r in [rows, ld) are written as zero (K padding of a transposed operand)
 template <typename E>
 __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ src, E* __restrict__ dst,
-                                                   int rows, int cols) {
+                                                   int rows, int cols, int ld) {
     __shared__ E tile[64][65];
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int r = ty; r < 64; r += 4) {
         const int gr = r0 + r, gc = c0 + tx;
-        if (gr < rows && gc < cols) tile[r][tx] = src[(int64_t)gr * cols + gc];
+        tile[r][tx] = (gr < rows && gc < cols) ? src[(int64_t)gr * cols + gc] : E(0);
     }
     __syncthreads();
     for (int c = ty; c < 64; c += 4) {
         const int gc = c0 + c, gr = r0 + tx;
-        if (gc < cols && gr < rows) dst[(int64_t)gc * rows + gr] = tile[tx][c];
+        if (gc < cols && gr < ld) dst[(int64_t)gc * ld + gr] = tile[tx][c];
     }
 }
 
-hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int cols, hipStream_t s) {
-    dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int cols, hipStream_t s, int ld) {
+    if (ld < rows) ld = rows;
+    dim3 grid((cols + 63) / 64, (ld + 63) / 64);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows, cols);
+                           static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows, cols, ld);
     else
         hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s,
-                           static_cast<const float*>(src), static_cast<float*>(dst), rows, cols);
+                           static_cast<const float*>(src), static_cast<float*>(dst), rows, cols, ld);
     return hipGetLastError();
 }
 

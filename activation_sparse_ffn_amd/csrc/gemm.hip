@@ -20,7 +20,8 @@
 
 namespace sffn {
 
-enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_GATEUP = 2, EPI_PARTIAL = 3, EPI_TOPK = 4, EPI_AMP = 5 };
+enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_GATEUP = 2, EPI_PARTIAL = 3, EPI_TOPK = 4, EPI_AMP = 5,
+       EPI_F32_ACC = 6, EPI_UV = 7 };
 
 struct GemmParams {
     const uint16_t* A;   // [M, K]
@@ -43,6 +44,7 @@ struct GemmParams {
     uint16_t* gate_w;    // fp16 gate tiles
     int keep;
     int dense;           // EPI_GATEUP without gate tiles: every channel kept (silu gate)
+    float* Cf2;          // EPI_UV: fp32 [M, N] receives V (Cf receives U)
 };
 
 constexpr int BM = 128, BN = 128, BK = 32;
@@ -64,7 +66,7 @@ constexpr int SLAB128 = BM * TKD * 2;    // one 128-row slab: 16 KB
 // the register-staged loop with 32-wide K steps.
 template <int EPI, bool DMA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_TOPK ? 2 : 1))) void k_gemm(const GemmParams p) {
-    constexpr int NB = (EPI == EPI_GATEUP) ? 2 : 1;
+    constexpr int NB = (EPI == EPI_GATEUP || EPI == EPI_UV) ? 2 : 1;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -331,6 +333,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
                     p.Cb[o] = f32_to_bf16(acc[0][i][j][v]);
                 } else if constexpr (EPI == EPI_F32_BIAS) {
                     p.Cf[o] = acc[0][i][j][v] + (p.bias ? p.bias[n] : 0.f);
+                } else if constexpr (EPI == EPI_F32_ACC) {
+                    p.Cf[o] += acc[0][i][j][v];
+                } else if constexpr (EPI == EPI_UV) {
+                    p.Cf[o] = acc[0][i][j][v];
+                    p.Cf2[o] = acc[NB - 1][i][j][v];
                 } else {
                     const float u = acc[0][i][j][v];
                     const float vv = acc[NB - 1][i][j][v];
@@ -363,7 +370,7 @@ constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab 
 template <int EPI, int WN>
 __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
     // WN waves along N (2 or 4), 2 along M: each wave owns 128 x (256 / WN) of C
-    constexpr bool GU = EPI == EPI_GATEUP || EPI == EPI_AMP;   // B = [W_g, W_u] blocks
+    constexpr bool GU = EPI == EPI_GATEUP || EPI == EPI_AMP || EPI == EPI_UV;   // B = [W_g, W_u] blocks
     constexpr int NT = 128 * WN;                     // threads
     constexpr int WNC = TN / WN;                      // columns per wave
     constexpr int NJ = WNC / 32;                      // accumulator tiles along N
@@ -635,6 +642,11 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
                     p.Cb[o] = f32_to_bf16(acc[i][j][v]);
                 } else if constexpr (EPI == EPI_F32_BIAS) {
                     p.Cf[o] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.f);
+                } else if constexpr (EPI == EPI_F32_ACC) {
+                    p.Cf[o] += acc[i][j][v];
+                } else if constexpr (EPI == EPI_UV) {
+                    p.Cf[o] = acc[i][j][v];
+                    p.Cf2[o] = acc[i][j + NJ / 2][v];
                 } else {
                     const float u = acc[i][j][v];
                     const float vv = acc[i][j + NJ / 2][v];
@@ -654,7 +666,7 @@ template <int EPI>
 static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
     constexpr int WN = SFFN_GEMM256_WN;
     const int m_tiles = (int)((p.M + TM - 1) / TM);
-    constexpr int TNC = (EPI == EPI_GATEUP || EPI == EPI_AMP) ? TN / 2 : TN;
+    constexpr int TNC = (EPI == EPI_GATEUP || EPI == EPI_AMP || EPI == EPI_UV) ? TN / 2 : TN;
     const int n_tiles = (p.N + TNC - 1) / TNC;
     xlaunch(events, stage, k_gemm256<EPI, WN>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0, s, p,
             m_tiles, n_tiles);
@@ -767,6 +779,36 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
     if (big) gemm256<EPI_BF16>(g, s, a.events, 4);
     else gemm<EPI_BF16>(g, s, a.events, 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int64_t M, int N, int K, void* C,
+                          GemmOut out, hipStream_t s, const float* bias) {
+    GemmParams g{};
+    g.A = A; g.B0 = B; g.M = M; g.N = N; g.K = K; g.bias = bias;
+    const bool big = M >= 256 && K % TK == 0;
+    if (out == GemmOut::BF16) {
+        g.Cb = static_cast<uint16_t*>(C);
+        if (big) gemm256<EPI_BF16>(g, s, nullptr, 0);
+        else gemm<EPI_BF16>(g, s, nullptr, 0);
+    } else if (out == GemmOut::F32) {
+        g.Cf = static_cast<float*>(C);
+        if (big) gemm256<EPI_F32_BIAS>(g, s, nullptr, 0);
+        else gemm<EPI_F32_BIAS>(g, s, nullptr, 0);
+    } else {
+        g.Cf = static_cast<float*>(C);
+        if (big) gemm256<EPI_F32_ACC>(g, s, nullptr, 0);
+        else gemm<EPI_F32_ACC>(g, s, nullptr, 0);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_uv_gemm(const uint16_t* x, const uint16_t* W_g, const uint16_t* W_u, int64_t T, int d_i,
+                          int d, float* U, float* V, hipStream_t s) {
+    GemmParams g{};
+    g.A = x; g.B0 = W_g; g.B1 = W_u; g.M = T; g.N = d_i; g.K = d; g.Cf = U; g.Cf2 = V;
+    if (T >= 256 && d % TK == 0) gemm256<EPI_UV>(g, s, nullptr, 0);
+    else gemm<EPI_UV>(g, s, nullptr, 0);
     return hipGetLastError();
 }
 

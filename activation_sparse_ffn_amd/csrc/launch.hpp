@@ -134,7 +134,41 @@ size_t skinny_partial_floats(int64_t T, int d, int rank, int d_i);
 hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t s);
 
 // ---- packing ---------------------------------------------------------------
+// dst [cols][ld] = src [rows][cols] transposed; dst entries [rows, ld) of each
+// row are zero (ld <= rows: ld = rows)
 hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int cols,
-                            hipStream_t s);
+                            hipStream_t s, int ld = 0);
+
+// ---- plain GEMMs for the backward pass --------------------------------------
+// C[M, N] (row stride N) = A[M, K] B[N, K]^T, bf16 operands (K contiguous),
+// fp32 accumulation; K must be a multiple of 32
+enum class GemmOut { F32, F32_ACC, BF16 };   // store fp32, add to fp32, store bf16
+hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int64_t M, int N, int K, void* C,
+                          GemmOut out, hipStream_t s, const float* bias = nullptr);
+// dense U = X W_g^T and V = X W_u^T, fp32 [T, d_i] each
+hipError_t launch_uv_gemm(const uint16_t* x, const uint16_t* W_g, const uint16_t* W_u, int64_t T, int d_i,
+                          int d, float* U, float* V, hipStream_t s);
+
+// ---- backward pass (bf16 layers, predictor or silu gate) ----------------------
+struct BwdArgs {
+    int d, d_i, rank, keep, gate;
+    int64_t T;
+    float inv_tau;                  // 1 / tau (0: no surrogate term)
+    const uint16_t* x;              // [T, d]
+    const uint16_t* g_y;            // [T, d]
+    const uint64_t* mask;           // [T, d_i/64] the forward's mask
+    const uint16_t* A;              // [rank, d]
+    const uint16_t* B;              // [d_i, rank]
+    const float* bias;              // [d_i] or null
+    const uint16_t* W_g;            // [d_i, d]
+    const uint16_t* W_u;            // [d_i, d]
+    const uint16_t* W_dT;           // [d_i, d]
+    float *g_x, *g_A, *g_B, *g_bias, *g_Wg, *g_Wu, *g_Wd;   // outputs (g_bias may be null)
+    void* ws;                       // workspace of backward_workspace_bytes(...)
+};
+size_t backward_workspace_bytes(int64_t T, int d, int d_i, int rank);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+// x[0 .. n) = 0
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s);
 
 }  // namespace sffn

@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["topk", "copy"], default="decode")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["topk", "copy", "backward"], default="decode")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's bounded CPU sample")
@@ -229,6 +229,66 @@ def topk_stress(args):
                                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}), flush=True)
 
 
+def backward_bench(args):
+    """One backward pass (soft surrogate through the bank top-k) of a
+    4096-token chunk of the full layer, rotating 2 layers; executed TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_amd as sffn
+    import workloads as wl
+
+    T, n_layers = 4096, args.layers or 2
+    shape = wl.FULL
+    d, d_i, r = shape.d, shape.d_i, shape.rank
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t0 = time.time()
+    ffns = []
+    for li in range(n_layers):
+        L = wl.make_layer(shape, seed=li)
+        ffns.append(sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B), None,
+                                   keep=args.keep, gate=args.gate))
+        del L
+    x = dev(wl.make_tokens(shape, T, seed=1, outlier_frac=0.01))
+    gy = dev(wl.make_tokens(shape, T, seed=2))
+    masks = []
+    for f in ffns:
+        _, m = f(x, return_mask=True)
+        masks.append(m)
+    ws = torch.empty(ffns[0]._lib.sparse_ffn_backward_workspace_size(ffns[0]._h, T), dtype=torch.uint8,
+                     device="cuda")
+    log(f"setup {time.time() - t0:.1f}s, backward workspace {ws.numel() / 2**30:.2f} GiB")
+    K, W = max(1, min(args.steps, 64)), max(1, min(args.warmup, 8))
+    for i in range(W):
+        ffns[i % n_layers].backward(x, gy, masks[i % n_layers], workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        ffns[i % n_layers].backward(x, gy, masks[i % n_layers], workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    # executed: recomputed z, p, U and V; g_h; the weight gradients; g_z, g_A; g_x
+    fl = 2 * T * (d * r + r * d_i + 2 * d * d_i + d * d_i + d * d_i + 2 * d * d_i
+                  + d_i * r + d_i * r + r * d + d * r + 2 * d * d_i)
+    tf = fl / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "sparse-FFN backward (soft surrogate top-k), 4096-token chunk",
+                      "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+                      "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+                      "config": {"workload": f"backward: {T} tokens, d={d}, d_i={d_i}, rank={r}, "
+                                             f"keep {args.keep} of 64, gate {args.gate}, tau 1",
+                                 "layers_rotated": n_layers},
+                      "executed_flops": fl,
+                      "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -251,6 +311,9 @@ def main():
         return
     if args.workload == "topk":
         topk_stress(args)
+        return
+    if args.workload == "backward":
+        backward_bench(args)
         return
     cfg = WORKLOADS[args.workload]
     T = cfg["T"]

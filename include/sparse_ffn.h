@@ -165,6 +165,36 @@ sffn_status_t sparse_ffn_set_stage_events(sffn_handle_t h, void* const* events,
  * gate these are the predictor and top-k stages); NULL when out of range. */
 const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i);
 
+/* Workspace bytes sparse_ffn_backward needs for T tokens (0 for T <= 0 or
+ * a null handle). About 10 fp32/bf16 [T, d_i] buffers plus the transposed
+ * weights: ~2.4 GB at T = 4096, d = 4096, d_i = 14336. */
+size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T);
+
+/* Backward pass of a forward of T tokens ("Continual LLM Upcycling",
+ * gist.science technical summary, Methodologie > 1. Architectuur, Executie >
+ * Backward Pass: the top-k is crossed by a soft, sigmoid-like local
+ * gradient around the selection threshold so that the loss reaches the
+ * predictor). Gradients of L = sum(y * g_y):
+ *   x, g_y  [T, d] bf16 (device): the forward's input and dL/dy
+ *   mask    [T, d_i/64] uint64 (device): the mask the forward returned
+ *   tau     > 0: temperature of the surrogate (INFINITY: no surrogate term)
+ *   g_x [T, d], g_A [rank, d], g_B [d_i, rank], g_W_g, g_W_u [d_i, d],
+ *   g_W_d [d, d_i]: fp32 outputs (device, overwritten); g_bias [d_i] fp32 or
+ *   NULL (the layer's bias gradient; zeros for a layer without bias)
+ * The forward's hard mask is differentiated as sigmoid((p - theta) / tau),
+ * theta the midpoint of the bank's smallest kept and largest dropped logit
+ * (held constant); the mask gradient is taken for every channel, so gate and
+ * up are recomputed densely; z's bf16 rounding passes gradients unchanged;
+ * keep = 64 has no surrogate term. bf16 layers with the predictor or silu
+ * gate only (SFFN_ERR_UNSUPPORTED otherwise). Asynchronous on hip_stream;
+ * allocates nothing; T == 0 writes zero weight gradients (x, g_y, mask, g_x
+ * and the workspace may then be NULL). */
+sffn_status_t sparse_ffn_backward(sffn_handle_t h, const void* x, const void* g_y,
+                                  const uint64_t* mask, int64_t T, float tau,
+                                  float* g_x, float* g_A, float* g_B, float* g_bias,
+                                  float* g_Wg, float* g_Wu, float* g_Wd,
+                                  void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Free the handle (host memory only; `packed` stays the caller's). */
 void sparse_ffn_destroy(sffn_handle_t h);
 

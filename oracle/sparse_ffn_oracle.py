@@ -346,13 +346,17 @@ def _dsigmoid(a: np.ndarray) -> np.ndarray:
 
 def backward(x, A, B, W_g, W_u, W_d, g_y, bias=None, bank: int = 64, keep: int = 16,
              gate: str = "pred", tau: float = 1.0,
-             round_z_bf16: Optional[bool] = None) -> dict:
+             round_z_bf16: Optional[bool] = None,
+             mask_in: Optional[np.ndarray] = None) -> dict:
     """Gradients of L = sum(y * g_y) for every input of the layer.
 
     Returns g_x [T, d], g_A [rank, d], g_B [d_i, rank], g_bias [d_i] (or
     None), g_Wg, g_Wu [d_i, d], g_Wd [d, d_i], and the intermediates g_h,
     g_p, theta and the mask, all float64. ``tau = inf`` switches the
     surrogate term off (the derivative of the hard-mask forward).
+    ``mask_in`` (uint64 words) gives the forward's mask; theta is then the
+    midpoint of each bank's smallest kept and largest dropped logit, which is
+    the same value when the mask is the bank top-k of p.
     """
     if gate not in ("pred", "silu"):
         raise ValueError("gate must be 'pred' or 'silu'")
@@ -364,7 +368,10 @@ def backward(x, A, B, W_g, W_u, W_d, g_y, bias=None, bank: int = 64, keep: int =
     G = widen(g_y)
     # forward, as the forward pass computes it
     z, p32 = predictor_logits(x, A, B, bias, round_z_bf16)
-    m = bank_topk_mask(p32, bank, keep).astype(np.float64)
+    if mask_in is None:
+        m = bank_topk_mask(p32, bank, keep).astype(np.float64)
+    else:
+        m = words_to_mask(np.asarray(mask_in), bank).astype(np.float64)
     p = p32.astype(np.float64)
     U = X @ Wg.T
     V = X @ Wu.T
@@ -383,7 +390,12 @@ def backward(x, A, B, W_g, W_u, W_d, g_y, bias=None, bank: int = 64, keep: int =
     g_V = m * g_h * s * U
     # the surrogate gradient of the mask
     T, d_i = p.shape
-    theta = bank_threshold(p, bank, keep)
+    if mask_in is None:
+        theta = bank_threshold(p, bank, keep)
+    else:
+        key = np.where(np.isnan(p), -np.inf, p).reshape(T, d_i // bank, bank)
+        mb = m.reshape(T, d_i // bank, bank) > 0
+        theta = 0.5 * (np.where(mb, key, np.inf).min(-1) + np.where(mb, -np.inf, key).max(-1))
     if keep < bank and np.isfinite(tau):
         th = np.repeat(theta, bank, axis=1)
         g_m = g_h * s * U * V

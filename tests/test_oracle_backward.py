@@ -143,3 +143,20 @@ def test_threshold_and_full_bank():
     q = p.copy()
     q[0, 5] = np.nan                     # NaN ranks last: 4, 3, 2 | 1
     assert o.bank_threshold(q, 8, 3)[0, 0] == 1.5
+
+
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_mask_in_with_own_mask_is_identical(gate):
+    """Given its own mask, the backward's min-kept / max-dropped threshold
+    equals the sorted keep-th / (keep+1)-th midpoint, and every gradient
+    is unchanged."""
+    L, rng = _layer(8)
+    x = rng.standard_normal((6, 24)).astype(np.float32)
+    G = rng.standard_normal((6, 24))
+    args = (x, L["A"], L["B"], L["W_g"], L["W_u"], L["W_d"], G)
+    kw = dict(bias=L["bias"], bank=16, keep=5, gate=gate, tau=0.8, round_z_bf16=False)
+    r = o.backward(*args, **kw)
+    rp = o.backward(*args, mask_in=o.mask_to_words(r["mask"], 16), **kw)
+    np.testing.assert_array_equal(rp["theta"], r["theta"])
+    for k in ("g_x", "g_A", "g_B", "g_bias", "g_Wg", "g_Wu", "g_Wd"):
+        np.testing.assert_array_equal(rp[k], r[k])
