@@ -351,8 +351,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 
 // ---------------------------------------------------------------------------
 // 256 x 256 x 64 tiles for the large contractions (gate/up and down of a
-// prefill chunk). Four waves, each owning a 128 x 128 block of C as 4 x 4
-// accumulator tiles of v_mfma_f32_32x32x16_bf16. A K step moves a 256-row x
+// prefill chunk). 128 WN threads: WN waves along N and 2 along M, each
+// owning a 128 x (256 / WN) block of C as accumulator tiles of
+// v_mfma_f32_32x32x16_bf16. A K step moves a 256-row x
 // 128-byte slab of each operand: eight lanes per row (whole 128-byte lines),
 // into LDS with 16-byte chunks XOR-swizzled by row (chunk g of row r at slot
 // g ^ ((r >> 1) & 7), so that the 16 consecutive rows one fragment read
@@ -383,12 +384,23 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     const int r32 = lane & 31, hk = lane >> 5;
     const int kt_n = p.K / TK;
 
-    // Tile order: workgroups land on the 8 XCDs round-robin, so tile g runs on
-    // XCD g % 8; each XCD gets a contiguous run of tiles, M fastest, so the
-    // tiles sharing a B slab run side by side in one L2.
+    // Tile order: workgroups land on the 8 XCDs round-robin, so workgroup g
+    // runs on XCD g % 8; each XCD gets a contiguous run gx of the tile order,
+    // which walks groups of GM M-tiles, M fastest within a group. The 32
+    // tiles that one XCD runs side by side then form an 8 x 4 block: each A
+    // slab is shared by four of them and each B slab by eight in one L2
+    // (against 2 and 16 for a plain M-fastest order), which cuts the L2
+    // misses per K step by a third. Every 256 x 256 tile streams 64 KB per K
+    // step through its compute unit, and the misses' latency is what limits
+    // how fast that stream flows.
     const unsigned total = gridDim.x, g = blockIdx.x;
     const unsigned gx = (total % 8 == 0) ? (g % 8) * (total / 8) + g / 8 : g;
-    const int mt = (int)(gx % (unsigned)m_tiles), nt = (int)(gx / (unsigned)m_tiles);
+    constexpr int GM = 8;
+    const int grp = (int)(gx / (unsigned)(GM * n_tiles));
+    const int first_m = grp * GM;
+    const int gm = min(m_tiles - first_m, GM);
+    const int within = (int)(gx - (unsigned)grp * (unsigned)(GM * n_tiles));
+    const int mt = first_m + within % gm, nt = within / gm;
     const int64_t m0 = (int64_t)mt * TM;
     const int n0 = nt * TNC;
 
