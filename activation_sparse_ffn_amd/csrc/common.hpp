@@ -63,9 +63,16 @@ template <> struct Elem<float> {
 // Raw 16-byte words, loaded early and decoded later so that many loads are
 // in flight before the first use.
 template <typename T> struct Raw;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <> struct Raw<uint16_t> {
     uint4 w;
     __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+    // streaming load (nt): for data read once, so that it does not push
+    // reusable lines out of the caches
+    __device__ __forceinline__ void load_stream(const uint16_t* p) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        w = make_uint4(v.x, v.y, v.z, v.w);
+    }
     __device__ __forceinline__ void decode(float* o) const {
         o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x);
         o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);

@@ -9,9 +9,11 @@ kept rows, down on kept columns) over one batch of synthetic tokens already
 resident in HBM:
 
   decode   1 token per step (d = 4096, d_i = 14336, rank 448, 16 of 64 kept);
-           8 independently drawn layers are rotated and every step gets a
-           fresh token, so the ~105 MB a token touches are not served from
-           the 256 MB Infinity Cache. This is the default and the headline.
+           32 independently drawn layers (the depth of a model of this
+           width) are rotated and every step gets a fresh token, so neither
+           the ~105 MB a token touches nor the 16.5 MB of predictor weights
+           per layer (528 MB over the 32 layers) are served from the 256 MB
+           Infinity Cache. This is the default and the headline.
   batched  32 tokens per step, predictor output bias b ~ N(0, 0.5).
   prefill  4096 tokens per step with 1% outlier feature columns.
   topk     the bank top-k alone over 32768 x 14336 fp32 logits with 5% exact
@@ -43,7 +45,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 WORKLOADS = {
-    "decode": dict(T=1, layers=8, bias=False, outliers=0.0),
+    "decode": dict(T=1, layers=32, bias=False, outliers=0.0),
     "batched": dict(T=32, layers=8, bias=True, outliers=0.0),
     "prefill": dict(T=4096, layers=2, bias=False, outliers=0.01),
 }
