@@ -104,9 +104,17 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const bool valid = t < NB || (t - NB) * 32 + 8 * q + fr < p.M;
-                        w[u][t][q] = valid ? *reinterpret_cast<const uint4*>(src[t] + q * rstride8 + 64 * kstep(s_))
-                                           : make_uint4(0, 0, 0, 0);
+                        const uint16_t* at = src[t] + q * rstride8 + 64 * kstep(s_);
+                        if (t < NB) {
+                            // weight rows: read once per call, streamed past the caches
+                            Raw<uint16_t> rw;
+                            rw.load_stream(at);
+                            w[u][t][q] = rw.w;
+                        } else {
+                            // token rows: re-read by every workgroup from the L2
+                            const bool valid = (t - NB) * 32 + 8 * q + fr < p.M;
+                            w[u][t][q] = valid ? *reinterpret_cast<const uint4*>(at) : make_uint4(0, 0, 0, 0);
+                        }
                     }
             }
         }
