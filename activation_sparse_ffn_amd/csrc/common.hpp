@@ -102,7 +102,11 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float sigmoidf_dev(float a) { return 1.0f / (1.0f + __expf(-a)); }
+// 1 / (1 + e^-a) with the hardware reciprocal (1 ulp) instead of an IEEE
+// division: the division sequence cost ~12 instructions per value in the
+// top-k epilogue, which writes a sigmoid for every channel of the chunk.
+// a = -inf gives rcp(inf) = 0, a = +inf gives 1, NaN stays NaN.
+__device__ __forceinline__ float sigmoidf_dev(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // Order-preserving 32-bit key of a logit: larger value <=> larger key.
 // -0 and +0 share a key; every NaN gets key 0, below -inf (0x007fffff).
@@ -143,26 +147,26 @@ __device__ __forceinline__ uint64_t wave_bank_topk(uint32_t key, int keep) {
     return gt | __ballot(take);
 }
 
-// The 16th largest of 64 values: sort four groups of 16 (descending bitonic
-// networks), merge them pairwise keeping the top 16 (max against the other
+// The 16th largest of 64 values: sort four groups of 16 (Batcher's odd-even
+// merge sort, 63 compare-exchanges per group against 80 for a bitonic
+// network), merge them pairwise keeping the top 16 (max against the other
 // group reversed gives a bitonic sequence holding the top 16, which a
 // half-cleaner network sorts), and at the last level only the minimum of the
 // kept 16 is needed. The values hold no NaN, so max/min are plain compares.
 __device__ __forceinline__ void sort16_desc(float* a) {
 #pragma unroll
-    for (int sz = 2; sz <= 16; sz <<= 1)
+    for (int p = 1; p < 16; p <<= 1)
 #pragma unroll
-        for (int j = sz >> 1; j > 0; j >>= 1)
+        for (int k = p; k >= 1; k >>= 1)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const float x = a[i], y = a[l];
-                    const bool desc = (i & sz) == 0;
-                    a[i] = desc ? fmaxf(x, y) : fminf(x, y);
-                    a[l] = desc ? fminf(x, y) : fmaxf(x, y);
-                }
-            }
+            for (int j = k % p; j + k < 16; j += 2 * k)
+#pragma unroll
+                for (int i = 0; i < k; ++i)
+                    if (i + j + k < 16 && (i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+                        const float x = a[i + j], y = a[i + j + k];
+                        a[i + j] = fmaxf(x, y);
+                        a[i + j + k] = fminf(x, y);
+                    }
 }
 // a, b sorted descending -> a holds the top 16 of both, sorted descending
 __device__ __forceinline__ void merge_top16(float* a, const float* b) {

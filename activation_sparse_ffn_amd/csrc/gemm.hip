@@ -296,24 +296,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
         uint16_t* gp = p.gate_w + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
                                       (kGateTileRows * kGateTileCols) +
                        (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
+        // gate values: sigmoid(p) (predictor gate) or 1 (silu gate) where kept
+        auto pack = [&](auto gate_of) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float4 v0 = ld(2 * c), v1 = ld(2 * c + 1);
-            const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint32_t hw[4];
+            for (int c = 0; c < 8; ++c) {
+                const float4 v0 = ld(2 * c), v1 = ld(2 * c + 1);
+                const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hw[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint16_t h2[2];
+                for (int e = 0; e < 4; ++e) {
+                    uint16_t h2[2];
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int ch = 8 * c + 2 * e + k;
-                    const float gv = p.gate ? 1.f : sigmoidf_dev(pv[2 * e + k]);
-                    h2[k] = ((sel >> ch) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)gv) : kGateDropped;
+                    for (int k = 0; k < 2; ++k) {
+                        const int ch = 8 * c + 2 * e + k;
+                        const float gv = gate_of(pv[2 * e + k]);
+                        h2[k] = ((sel >> ch) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)gv) : kGateDropped;
+                    }
+                    hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
                 }
-                hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+                *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             }
-            *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        }
+        };
+        if (p.gate) pack([](float) { return 1.f; });
+        else pack([](float v) { return sigmoidf_dev(v); });
         return;
     }
 #pragma unroll
