@@ -23,6 +23,8 @@
 // Every product runs as C = A B^T on the MFMA GEMMs; operands that the
 // tokens must contract over are transposed first, zero-padded to a multiple
 // of 64 tokens.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -121,7 +123,15 @@ BwdLayout layout(int64_t T, int d, int d_i, int r) {
     L.z16 = take((size_t)T * r * 2);
     L.p32 = take(tdi * 4);
     L.gh32 = take(tdi * 4);
-    L.U32 = take(tdi * 4);
+    // U32 is dead outside [UV GEMM, k_bwd_bank]: the other GEMMs use it for
+    // their K-split partials
+    const int64_t Tq = (int64_t)Tp;
+    const size_t part = std::max({gemm_nt_partial_floats(T, r, d), gemm_nt_partial_floats(T, d_i, r),
+                                  gemm_nt_partial_floats(T, d_i, d), gemm_nt_partial_floats(d, d_i, (int)Tq),
+                                  gemm_nt_partial_floats(d_i, d, (int)Tq), gemm_nt_partial_floats(d_i, r, (int)Tq),
+                                  gemm_nt_partial_floats(T, r, d_i), gemm_nt_partial_floats(r, d, (int)Tq),
+                                  gemm_nt_partial_floats(T, d, r), gemm_nt_partial_floats(T, d, d_i)});
+    L.U32 = take(std::max(tdi, part) * 4);
     L.V32 = take(tdi * 4);
     L.h16 = take(tdi * 2);
     L.gu16 = take(tdi * 2);
@@ -186,9 +196,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; return e == hipSuccess; };
 
     // recomputed forward: z, p, dense U and V; g_h for every channel
-    ok(launch_gemm_nt(a.x, a.A, T, r, d, z16, GemmOut::BF16, s));
-    ok(launch_gemm_nt(z16, a.B, T, d_i, r, p32, GemmOut::F32, s, a.bias));
-    ok(launch_gemm_nt(a.g_y, a.W_dT, T, d_i, d, gh32, GemmOut::F32, s));
+    ok(launch_gemm_nt(a.x, a.A, T, r, d, z16, GemmOut::BF16, s, nullptr, U32));
+    ok(launch_gemm_nt(z16, a.B, T, d_i, r, p32, GemmOut::F32, s, a.bias, U32));
+    ok(launch_gemm_nt(a.g_y, a.W_dT, T, d_i, d, gh32, GemmOut::F32, s, nullptr, U32));
     ok(launch_uv_gemm(a.x, a.W_g, a.W_u, T, d_i, d, U32, V32, s));
     hipLaunchKernelGGL(k_bwd_bank, dim3((unsigned)((T * nb + 3) / 4)), dim3(256), 0, s, p32, U32, V32, gh32,
                        a.mask, T * nb, nb, a.gate, a.keep, a.inv_tau, h16, gu16, gv16, gp32, gp16);
@@ -205,22 +215,22 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     ok(launch_transpose(Dt::BF16, gv16, gvT, (int)T, d_i, s, Tp));
     ok(launch_transpose(Dt::BF16, gp16, gpT, (int)T, d_i, s, Tp));
     ok(launch_transpose(Dt::BF16, z16, zT, (int)T, r, s, Tp));
-    ok(launch_gemm_nt(GT, hT, d, d_i, Tp, a.g_Wd, GemmOut::F32, s));
-    ok(launch_gemm_nt(guT, XT, d_i, d, Tp, a.g_Wg, GemmOut::F32, s));
-    ok(launch_gemm_nt(gvT, XT, d_i, d, Tp, a.g_Wu, GemmOut::F32, s));
-    ok(launch_gemm_nt(gpT, zT, d_i, r, Tp, a.g_B, GemmOut::F32, s));
+    ok(launch_gemm_nt(GT, hT, d, d_i, Tp, a.g_Wd, GemmOut::F32, s, nullptr, U32));
+    ok(launch_gemm_nt(guT, XT, d_i, d, Tp, a.g_Wg, GemmOut::F32, s, nullptr, U32));
+    ok(launch_gemm_nt(gvT, XT, d_i, d, Tp, a.g_Wu, GemmOut::F32, s, nullptr, U32));
+    ok(launch_gemm_nt(gpT, zT, d_i, r, Tp, a.g_B, GemmOut::F32, s, nullptr, U32));
     // the predictor's input side
     ok(launch_transpose(Dt::BF16, a.B, BT, d_i, r, s));
-    ok(launch_gemm_nt(gp16, BT, T, r, d_i, gz16, GemmOut::BF16, s));
+    ok(launch_gemm_nt(gp16, BT, T, r, d_i, gz16, GemmOut::BF16, s, nullptr, U32));
     ok(launch_transpose(Dt::BF16, gz16, gzT, (int)T, r, s, Tp));
-    ok(launch_gemm_nt(gzT, XT, r, d, Tp, a.g_A, GemmOut::F32, s));
+    ok(launch_gemm_nt(gzT, XT, r, d, Tp, a.g_A, GemmOut::F32, s, nullptr, U32));
     // g_x = g_z A + g_u W_g + g_v W_u
     ok(launch_transpose(Dt::BF16, a.A, AT, r, d, s));
     ok(launch_transpose(Dt::BF16, a.W_g, WgT, d_i, d, s));
     ok(launch_transpose(Dt::BF16, a.W_u, WuT, d_i, d, s));
-    ok(launch_gemm_nt(gz16, AT, T, d, r, a.g_x, GemmOut::F32, s));
-    ok(launch_gemm_nt(gu16, WgT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s));
-    ok(launch_gemm_nt(gv16, WuT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s));
+    ok(launch_gemm_nt(gz16, AT, T, d, r, a.g_x, GemmOut::F32, s, nullptr, U32));
+    ok(launch_gemm_nt(gu16, WgT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, U32));
+    ok(launch_gemm_nt(gv16, WuT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, U32));
     return e;
 }
 

@@ -799,11 +799,60 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// How launch_gemm_nt runs C = A B^T: 0 = the 256 x 256 kernel, which needs
+// enough tiles to fill the chip; else the 128 x 128 kernel over that many K
+// ranges (> 1: fp32 partials, then their sum in a fixed order). Thin GEMMs
+// (one side the predictor rank) have only a few dozen 256 x 256 tiles.
+static int nt_splits(int64_t M, int N, int K) {
+    const int64_t t256 = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+    if (M >= TM && K % TK == 0 && t256 >= 192) return 0;
+    const int64_t t128 = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int sp = 1;
+    while (t128 * sp < 512 && K % (2 * sp * TKD) == 0 && K / (2 * sp) >= 256) sp *= 2;
+    return sp;
+}
+
+size_t gemm_nt_partial_floats(int64_t M, int N, int K) {
+    const int sp = nt_splits(M, N, K);
+    return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N : 0;
+}
+
+// C = (sum of the K-split partials in order) (+ bias[col]), stored as bf16,
+// stored as fp32 or added to fp32
+__global__ __launch_bounds__(256) void k_sum_splits_out(const float* __restrict__ partial, void* __restrict__ C,
+                                                        int splits, int64_t n, int N, int mode,
+                                                        const float* __restrict__ bias) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.f;
+    for (int k = 0; k < splits; ++k) acc += partial[(size_t)k * n + i];
+    if (bias) acc += bias[i % N];
+    if (mode == 2) static_cast<uint16_t*>(C)[i] = f32_to_bf16(acc);
+    else if (mode == 1) static_cast<float*>(C)[i] += acc;
+    else static_cast<float*>(C)[i] = acc;
+}
+
 hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int64_t M, int N, int K, void* C,
-                          GemmOut out, hipStream_t s, const float* bias) {
+                          GemmOut out, hipStream_t s, const float* bias, float* partial) {
     GemmParams g{};
     g.A = A; g.B0 = B; g.M = M; g.N = N; g.K = K; g.bias = bias;
-    const bool big = M >= 256 && K % TK == 0;
+    const int sp = nt_splits(M, N, K);
+    if (sp > 1 && partial != nullptr) {
+        g.Cf = partial; g.kn = K / sp;
+        const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        if (g.kn % TKD == 0)
+            hipExtLaunchKernelGGL(k_gemm<EPI_PARTIAL, true>, dim3((unsigned)tiles, (unsigned)sp), dim3(256), 0, s,
+                                  nullptr, nullptr, 0u, g);
+        else
+            hipExtLaunchKernelGGL(k_gemm<EPI_PARTIAL, false>, dim3((unsigned)tiles, (unsigned)sp), dim3(256), 0, s,
+                                  nullptr, nullptr, 0u, g);
+        const int64_t n = M * (int64_t)N;
+        const int mode = out == GemmOut::BF16 ? 2 : out == GemmOut::F32_ACC ? 1 : 0;
+        hipLaunchKernelGGL(k_sum_splits_out, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           (const float*)partial, C, sp, n, N, mode, bias);
+        return hipGetLastError();
+    }
+    const bool big = sp == 0;
     if (out == GemmOut::BF16) {
         g.Cb = static_cast<uint16_t*>(C);
         if (big) gemm256<EPI_BF16>(g, s, nullptr, 0);

@@ -140,11 +140,14 @@ hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int col
                             hipStream_t s, int ld = 0);
 
 // ---- plain GEMMs for the backward pass --------------------------------------
-// C[M, N] (row stride N) = A[M, K] B[N, K]^T, bf16 operands (K contiguous),
-// fp32 accumulation; K must be a multiple of 32
+// C[M, N] (row stride N) = A[M, K] B[N, K]^T (+ bias[col] for F32), bf16
+// operands (K contiguous), fp32 accumulation; K must be a multiple of 32.
+// Thin shapes split K when `partial` holds gemm_nt_partial_floats(M, N, K)
+// floats (null: no split).
 enum class GemmOut { F32, F32_ACC, BF16 };   // store fp32, add to fp32, store bf16
+size_t gemm_nt_partial_floats(int64_t M, int N, int K);
 hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int64_t M, int N, int K, void* C,
-                          GemmOut out, hipStream_t s, const float* bias = nullptr);
+                          GemmOut out, hipStream_t s, const float* bias = nullptr, float* partial = nullptr);
 // dense U = X W_g^T and V = X W_u^T, fp32 [T, d_i] each
 hipError_t launch_uv_gemm(const uint16_t* x, const uint16_t* W_g, const uint16_t* W_u, int64_t T, int d_i,
                           int d, float* U, float* V, hipStream_t s);
