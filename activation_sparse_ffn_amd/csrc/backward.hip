@@ -16,13 +16,14 @@
 //   z = bf16(x A^T), p = z B^T + bias          recomputed forward logits
 //   g_h = g_y W_d                               every channel (W_d^T packed)
 //   U = x W_g^T, V = x W_u^T                    dense, fp32
-//   k_bwd_bank: theta, h, g_u, g_v, g_p         one wave per (token, bank)
+//   k_bwd_tile: theta, h, g_u, g_v, g_p         one workgroup per (64 tokens, bank)
 //   g_W_d = g_y^T h, g_W_g = g_u^T x, g_W_u = g_v^T x, g_B = g_p^T z,
 //   g_z = g_p B, g_A = g_z^T x, g_bias = sum_t g_p,
 //   g_x = g_z A + g_u W_g + g_v W_u
 // Every product runs as C = A B^T on the MFMA GEMMs; operands that the
-// tokens must contract over are transposed first, zero-padded to a multiple
-// of 64 tokens.
+// tokens must contract over are token-transposed, zero-padded to a multiple
+// of 64 tokens: h, g_u, g_v and g_p by k_bwd_tile itself, x, g_y, z and g_z
+// by a transpose kernel.
 #include <algorithm>
 
 #include "common.hpp"
@@ -41,43 +42,84 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// One wave per (token, bank), one channel per lane.
-__global__ __launch_bounds__(256) void k_bwd_bank(const float* __restrict__ p, const float* __restrict__ U,
+// One workgroup per (block of 64 tokens, bank): each wave takes 16 of the
+// tokens in turn, one channel per lane. g_u, g_v and g_p leave token-major
+// (the A operands of g_x and g_z); h, g_u, g_v and g_p also leave transposed
+// through LDS, [d_i][Tp] with zero columns past T (the operands of the
+// weight gradients, which contract over tokens); g_p's column sums over the
+// block go to colpart[block][d_i] for g_bias.
+constexpr int kBwdTok = 64;
+__global__ __launch_bounds__(256) void k_bwd_tile(const float* __restrict__ p, const float* __restrict__ U,
                                                   const float* __restrict__ V, const float* __restrict__ g_h,
-                                                  const uint64_t* __restrict__ mask, int64_t n_words, int nb,
+                                                  const uint64_t* __restrict__ mask, int64_t T, int nb, int Tp,
                                                   int gate, int keep, float inv_tau,
-                                                  uint16_t* __restrict__ h_out, uint16_t* __restrict__ g_u,
-                                                  uint16_t* __restrict__ g_v, float* __restrict__ g_p32,
-                                                  uint16_t* __restrict__ g_p16) {
+                                                  uint16_t* __restrict__ g_u, uint16_t* __restrict__ g_v,
+                                                  uint16_t* __restrict__ g_p16, uint16_t* __restrict__ hT,
+                                                  uint16_t* __restrict__ guT, uint16_t* __restrict__ gvT,
+                                                  uint16_t* __restrict__ gpT, float* __restrict__ colpart) {
+    constexpr int LD = kBwdTok + 8;                  // row pitch (elements) of the LDS tiles: 144 bytes
+    __shared__ __attribute__((aligned(16))) uint16_t tile[4][kBank][LD];
+    __shared__ float csum[4][kBank];
     const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w >= n_words) return;
-    const int64_t t = w / nb;
-    const int b = (int)(w - t * nb);
-    const int64_t o = t * (int64_t)nb * kBank + b * kBank + lane;
-    const float pv = p[o], u = U[o], v = V[o], gh = g_h[o];
-    const bool kept = (mask[w] >> lane) & 1ull;
-    const float m = kept ? 1.f : 0.f;
-    // threshold: midpoint of the smallest kept and the largest dropped logit
-    const float key = __builtin_isnan(pv) ? -__builtin_huge_valf() : pv;
-    const float kmin = wave_min(kept ? key : __builtin_huge_valf());
-    const float dmax = wave_max(kept ? -__builtin_huge_valf() : key);
-    const float sp = sigmoidf_dev(pv), su = sigmoidf_dev(u);
-    const float s = gate ? su : sp;
-    const float gm = gh * s * u * v;                 // dL/dm
-    const float gu = gate ? m * gh * v * (su + u * su * (1.f - su)) : m * gh * s * v;
-    const float gv = m * gh * s * u;
-    float gp = gate ? 0.f : m * gh * u * v * sp * (1.f - sp);
-    if (keep < kBank && inv_tau > 0.f) {
-        const float theta = 0.5f * (kmin + dmax);
-        const float sa = sigmoidf_dev((pv - theta) * inv_tau);
-        gp += gm * sa * (1.f - sa) * inv_tau;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tb = blockIdx.x, b = blockIdx.y;
+    const int d_i = nb * kBank;
+    const int j = b * kBank + lane;
+    float colp = 0.f;
+    for (int i = 0; i < kBwdTok / 4; ++i) {
+        const int tl = wv * (kBwdTok / 4) + i;       // token within the block
+        const int64_t t = (int64_t)tb * kBwdTok + tl;
+        uint16_t o_h = 0, o_u = 0, o_v = 0, o_p = 0;
+        if (t < T) {
+            const int64_t w = t * nb + b;
+            const int64_t o = t * (int64_t)d_i + j;
+            const float pv = p[o], u = U[o], v = V[o], gh = g_h[o];
+            const bool kept = (mask[w] >> lane) & 1ull;
+            const float m = kept ? 1.f : 0.f;
+            // threshold: midpoint of the smallest kept and the largest dropped logit
+            const float key = __builtin_isnan(pv) ? -__builtin_huge_valf() : pv;
+            const float kmin = wave_min(kept ? key : __builtin_huge_valf());
+            const float dmax = wave_max(kept ? -__builtin_huge_valf() : key);
+            const float sp = sigmoidf_dev(pv), su = sigmoidf_dev(u);
+            const float s = gate ? su : sp;
+            const float gm = gh * s * u * v;                 // dL/dm
+            const float gu = gate ? m * gh * v * (su + u * su * (1.f - su)) : m * gh * s * v;
+            const float gv = m * gh * s * u;
+            float gp = gate ? 0.f : m * gh * u * v * sp * (1.f - sp);
+            if (keep < kBank && inv_tau > 0.f) {
+                const float theta = 0.5f * (kmin + dmax);
+                const float sa = sigmoidf_dev((pv - theta) * inv_tau);
+                gp += gm * sa * (1.f - sa) * inv_tau;
+            }
+            colp += gp;
+            o_h = f32_to_bf16(m * s * u * v);
+            o_u = f32_to_bf16(gu);
+            o_v = f32_to_bf16(gv);
+            o_p = f32_to_bf16(gp);
+            g_u[o] = o_u;
+            g_v[o] = o_v;
+            g_p16[o] = o_p;
+        }
+        tile[0][lane][tl] = o_h;
+        tile[1][lane][tl] = o_u;
+        tile[2][lane][tl] = o_v;
+        tile[3][lane][tl] = o_p;
     }
-    h_out[o] = f32_to_bf16(m * s * u * v);
-    g_u[o] = f32_to_bf16(gu);
-    g_v[o] = f32_to_bf16(gv);
-    g_p32[o] = gp;
-    g_p16[o] = f32_to_bf16(gp);
+    csum[wv][lane] = colp;
+    __syncthreads();
+    if (wv == 0) colpart[(size_t)tb * d_i + j] = (csum[0][lane] + csum[1][lane]) + (csum[2][lane] + csum[3][lane]);
+    // transposed tiles: 64 channel rows of 128 bytes per output, 16 bytes per thread
+    uint16_t* const dst[4] = {hT, guT, gvT, gpT};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = threadIdx.x + 256 * k;            // 512 chunks: row c / 8, chunk c % 8
+            const int row = c >> 3, ch = c & 7;
+            const uint4 val = *reinterpret_cast<const uint4*>(&tile[q][row][8 * ch]);
+            *reinterpret_cast<uint4*>(dst[q] + (size_t)(b * kBank + row) * Tp + (size_t)tb * kBwdTok + 8 * ch) = val;
+        }
+    }
 }
 
 // out[c] = sum over rows of x[r][c] in a fixed order: thread (column,
@@ -110,7 +152,7 @@ constexpr size_t kWsAlign = 256;
 size_t up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 struct BwdLayout {
-    size_t z16, p32, gh32, U32, V32, h16, gu16, gv16, gp32, gp16, gz16;
+    size_t z16, p32, gh32, U32, V32, gu16, gv16, gp16, gz16, colpart;
     size_t GT, hT, XT, guT, gvT, gpT, zT, gzT, BT, AT, WgT, WuT, total;
 };
 
@@ -123,7 +165,7 @@ BwdLayout layout(int64_t T, int d, int d_i, int r) {
     L.z16 = take((size_t)T * r * 2);
     L.p32 = take(tdi * 4);
     L.gh32 = take(tdi * 4);
-    // U32 is dead outside [UV GEMM, k_bwd_bank]: the other GEMMs use it for
+    // U32 is dead outside [UV GEMM, k_bwd_tile]: the other GEMMs use it for
     // their K-split partials
     const int64_t Tq = (int64_t)Tp;
     const size_t part = std::max({gemm_nt_partial_floats(T, r, d), gemm_nt_partial_floats(T, d_i, r),
@@ -133,10 +175,9 @@ BwdLayout layout(int64_t T, int d, int d_i, int r) {
                                   gemm_nt_partial_floats(T, d, r), gemm_nt_partial_floats(T, d, d_i)});
     L.U32 = take(std::max(tdi, part) * 4);
     L.V32 = take(tdi * 4);
-    L.h16 = take(tdi * 2);
     L.gu16 = take(tdi * 2);
     L.gv16 = take(tdi * 2);
-    L.gp32 = take(tdi * 4);
+    L.colpart = take(Tp / 64 * (size_t)d_i * 4);
     L.gp16 = take(tdi * 2);
     L.gz16 = take((size_t)T * r * 2);
     L.GT = take((size_t)d * Tp * 2);
@@ -174,10 +215,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     float* gh32 = at<float>(ws, L.gh32);
     float* U32 = at<float>(ws, L.U32);
     float* V32 = at<float>(ws, L.V32);
-    uint16_t* h16 = at<uint16_t>(ws, L.h16);
     uint16_t* gu16 = at<uint16_t>(ws, L.gu16);
     uint16_t* gv16 = at<uint16_t>(ws, L.gv16);
-    float* gp32 = at<float>(ws, L.gp32);
+    float* colpart = at<float>(ws, L.colpart);
     uint16_t* gp16 = at<uint16_t>(ws, L.gp16);
     uint16_t* gz16 = at<uint16_t>(ws, L.gz16);
     uint16_t* GT = at<uint16_t>(ws, L.GT);
@@ -200,20 +240,18 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     ok(launch_gemm_nt(z16, a.B, T, d_i, r, p32, GemmOut::F32, s, a.bias, U32));
     ok(launch_gemm_nt(a.g_y, a.W_dT, T, d_i, d, gh32, GemmOut::F32, s, nullptr, U32));
     ok(launch_uv_gemm(a.x, a.W_g, a.W_u, T, d_i, d, U32, V32, s));
-    hipLaunchKernelGGL(k_bwd_bank, dim3((unsigned)((T * nb + 3) / 4)), dim3(256), 0, s, p32, U32, V32, gh32,
-                       a.mask, T * nb, nb, a.gate, a.keep, a.inv_tau, h16, gu16, gv16, gp32, gp16);
+    hipLaunchKernelGGL(k_bwd_tile, dim3((unsigned)(Tp / kBwdTok), (unsigned)nb), dim3(256), 0, s, p32, U32, V32,
+                       gh32, a.mask, T, nb, Tp, a.gate, a.keep, a.inv_tau, gu16, gv16, gp16, hT, guT, gvT, gpT,
+                       colpart);
     ok(hipGetLastError());
     if (a.g_bias) {
-        hipLaunchKernelGGL(k_colsum, dim3((unsigned)((d_i + 31) / 32)), dim3(256), 0, s, gp32, T, d_i, a.g_bias);
+        hipLaunchKernelGGL(k_colsum, dim3((unsigned)((d_i + 31) / 32)), dim3(256), 0, s, colpart,
+                           (int64_t)(Tp / kBwdTok), d_i, a.g_bias);
         ok(hipGetLastError());
     }
     // token-major operands transposed for the weight gradients (K = tokens)
     ok(launch_transpose(Dt::BF16, a.g_y, GT, (int)T, d, s, Tp));
-    ok(launch_transpose(Dt::BF16, h16, hT, (int)T, d_i, s, Tp));
     ok(launch_transpose(Dt::BF16, a.x, XT, (int)T, d, s, Tp));
-    ok(launch_transpose(Dt::BF16, gu16, guT, (int)T, d_i, s, Tp));
-    ok(launch_transpose(Dt::BF16, gv16, gvT, (int)T, d_i, s, Tp));
-    ok(launch_transpose(Dt::BF16, gp16, gpT, (int)T, d_i, s, Tp));
     ok(launch_transpose(Dt::BF16, z16, zT, (int)T, r, s, Tp));
     ok(launch_gemm_nt(GT, hT, d, d_i, Tp, a.g_Wd, GemmOut::F32, s, nullptr, U32));
     ok(launch_gemm_nt(guT, XT, d_i, d, Tp, a.g_Wg, GemmOut::F32, s, nullptr, U32));
