@@ -48,6 +48,7 @@ struct GemmParams {
 };
 
 constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int kTopkPitch = 64 * 4 + 16;   // bytes per bank-row of the top-k epilogue's logit tile
 constexpr int LDS_STRIDE = BK + 8;   // elements; 80-byte rows keep 16-byte alignment
 
 // LDS slab layout shared by the LDS-direct loops: a slab holds rows of 64
@@ -99,14 +100,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
                 for (int j = 0; j < 2; ++j)
                     acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
     };
-    // EPI_TOPK: the fp32 logit tile as 256 bank-rows of 256 bytes, rows
-    // 0..127 in `tile_lo`, 128..255 in `tile_hi` (the freed staging buffers)
+    // EPI_TOPK: the fp32 logit tile as 256 bank-rows (64 floats + 16 bytes of
+    // padding), rows 0..127 in `tile_lo`, 128..255 in `tile_hi` (the freed
+    // staging buffers, enlarged to hold them)
+    constexpr int TOPK_HALF = 128 * kTopkPitch;
     char* tile_lo;
     char* tile_hi;
 
     if constexpr (DMA) {
-        __shared__ __attribute__((aligned(16))) char buf0[(1 + NB) * SLAB128];
-        __shared__ __attribute__((aligned(16))) char buf1[(1 + NB) * SLAB128];
+        constexpr int BUF = (EPI == EPI_TOPK && TOPK_HALF > (1 + NB) * SLAB128) ? TOPK_HALF : (1 + NB) * SLAB128;
+        __shared__ __attribute__((aligned(16))) char buf0[BUF];
+        __shared__ __attribute__((aligned(16))) char buf1[BUF];
         // per-thread fetch rows: chunk c = tid + 256 i -> row c / 8, slot c % 8
         // (lane l of a wave lands at base + 16 l). Rows past M or N read row
         // 0: their results are never stored.
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
         tile_hi = buf1;
     } else {
         constexpr int STAGE_BYTES = (BM + NB * BN) * LDS_STRIDE * 2;
-        constexpr int TILE_BYTES = EPI == EPI_TOPK ? BM * BN * 4 : 0;     // fp32 logits tile
+        constexpr int TILE_BYTES = EPI == EPI_TOPK ? 2 * TOPK_HALF : 0;   // fp32 logits tile
         __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > TILE_BYTES ? STAGE_BYTES : TILE_BYTES];
         uint16_t* const As = reinterpret_cast<uint16_t*>(smem);
         auto BS = [&](int b) { return As + (BM + b * BN) * LDS_STRIDE; };
@@ -252,16 +256,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
             __syncthreads();
         }
         tile_lo = smem;
-        tile_hi = smem + 128 * 256;
+        tile_hi = smem + TOPK_HALF;
     }
 
     // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2) + 4 (lane >> 5)
     const int nb64 = p.N / kBank;
     if constexpr (EPI == EPI_TOPK) {
-        // logits (+ bias) into LDS as 256 bank-rows q = 2 row + (col >> 6) of
-        // 256 bytes, 16-byte chunks swizzled by q; the staging buffers are free
-        // (the K loop ended on a barrier)
-        auto tile_row = [&](int q) { return (q < 128 ? tile_lo : tile_hi) + (q & 127) * 256; };
+        // logits (+ bias) into LDS as 256 bank-rows q = 2 row + (col >> 6),
+        // kTopkPitch bytes apart; the staging buffers are free (the K loop
+        // ended on a barrier). Wave wm holds rows 64 wm .. 64 wm + 63, all in
+        // one half, and a value's address is a per-lane base plus a constant,
+        // so the stores need no address arithmetic. The 16-byte padding puts
+        // the two rows one store instruction touches (lanes 0-31 and 32-63,
+        // rows 4 apart) on disjoint banks, and the 16 bank-rows of one quarter
+        // of a 16-byte-per-lane read on distinct banks.
+        char* const half = wm == 0 ? tile_lo : tile_hi;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -269,13 +278,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
                 const int col = wn * 64 + j * 32 + (lane & 31);
                 const int n = n0 + col;
                 const float bj = (p.bias && n < p.N) ? p.bias[n] : 0.f;
+                char* const base = half + (2 * (i * 32 + 4 * hk) + (col >> 6)) * kTopkPitch + (col & 63) * 4;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 64 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * (lane >> 5);
-                    const int q = 2 * row + (col >> 6), c64 = col & 63;
-                    *reinterpret_cast<float*>(tile_row(q) + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
+                for (int v = 0; v < 16; ++v)
+                    *reinterpret_cast<float*>(base + (2 * ((v & 3) + 8 * (v >> 2))) * kTopkPitch) =
                         acc[0][i][j][v] + bj;
-                }
             }
         __syncthreads();
         // one bank-row per lane
@@ -283,8 +290,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
         const int row = q >> 1, bsel = q & 1;
         const int64_t t = m0 + row;
         const int j0 = n0 + bsel * kBank;
-        const char* trow = tile_row(q);
-        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(trow + ((c ^ (q & 15)) << 4)); };
+        const char* trow = (q < 128 ? tile_lo : tile_hi) + (q & 127) * kTopkPitch;
+        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(trow + 16 * c); };
         const uint64_t sel = lane_select64(ld, p.keep);
         if (t >= p.M || j0 >= p.N) return;
         p.mask_w[t * nb64 + j0 / kBank] = sel;
