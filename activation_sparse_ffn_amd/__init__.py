@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "sparse_ffn_backward_workspace_size", "sparse_ffn_backward",
 )
 SFFN_STAGES = 5
+SFFN_FLAG_BACKWARD = 1
 
 
 class SparseFFNError(RuntimeError):
@@ -51,7 +52,7 @@ class SparseFFNError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("d_i", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("bank", ctypes.c_int32), ("keep", ctypes.c_int32), ("dtype", ctypes.c_int),
-                ("gate", ctypes.c_int)]
+                ("gate", ctypes.c_int), ("flags", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -154,10 +155,13 @@ class SparseFFN:
     buffer the object owns; the originals may be dropped afterwards.
     """
 
-    def __init__(self, W_g, W_u, W_d, A=None, B=None, bias=None, keep: int = 16, gate: str = "pred"):
+    def __init__(self, W_g, W_u, W_d, A=None, B=None, bias=None, keep: int = 16, gate: str = "pred",
+                 for_backward: bool = False):
         """gate: "pred" (sigmoid of the predictor logit), "silu" (sigmoid of
         u) or "amplitude" (the Dense-4x post-hoc baseline: no predictor, the
-        mask ranks |SiLU(u) v|; A and B may then be None)."""
+        mask ranks |SiLU(u) v|; A and B may then be None). for_backward: keep
+        W_g^T and W_u^T in the packed buffer (SFFN_FLAG_BACKWARD) so that
+        backward() does not transpose them on every call."""
         self._lib = load_library()
         if gate not in GATES:
             raise ValueError("gate must be 'pred', 'silu' or 'amplitude'")
@@ -180,7 +184,7 @@ class SparseFFN:
         self.device = W_g.device
         self.dtype = dt
         self.cfg = Config(d, d_i, rank, 64, keep, SFFN_BF16 if dt == torch.bfloat16 else SFFN_F32,
-                          GATES[gate])
+                          GATES[gate], SFFN_FLAG_BACKWARD if for_backward else 0)
         size = self._lib.sparse_ffn_packed_size(ctypes.byref(self.cfg))
         if size == 0:
             _check(self._lib, SFFN_ERR_INVALID_ARG)

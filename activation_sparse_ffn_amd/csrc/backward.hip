@@ -156,7 +156,7 @@ struct BwdLayout {
     size_t GT, hT, XT, guT, gvT, gpT, zT, gzT, BT, AT, WgT, WuT, total;
 };
 
-BwdLayout layout(int64_t T, int d, int d_i, int r) {
+BwdLayout layout(int64_t T, int d, int d_i, int r, bool weights_t) {
     const size_t Tp = (size_t)((T + 63) / 64 * 64);
     const size_t tdi = (size_t)T * d_i;
     BwdLayout L{};
@@ -190,8 +190,11 @@ BwdLayout layout(int64_t T, int d, int d_i, int r) {
     L.gzT = take((size_t)r * Tp * 2);
     L.BT = take((size_t)r * d_i * 2);
     L.AT = take((size_t)d * r * 2);
-    L.WgT = take((size_t)d * d_i * 2);
-    L.WuT = take((size_t)d * d_i * 2);
+    L.WgT = L.WuT = 0;
+    if (!weights_t) {
+        L.WgT = take((size_t)d * d_i * 2);
+        L.WuT = take((size_t)d * d_i * 2);
+    }
     L.total = off;
     return L;
 }
@@ -202,13 +205,16 @@ P* at(void* base, size_t off) {
 }
 }  // namespace
 
-size_t backward_workspace_bytes(int64_t T, int d, int d_i, int rank) { return layout(T, d, d_i, rank).total; }
+size_t backward_workspace_bytes(int64_t T, int d, int d_i, int rank, bool weights_t) {
+    return layout(T, d, d_i, rank, weights_t).total;
+}
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     const int64_t T = a.T;
     const int d = a.d, d_i = a.d_i, r = a.rank, nb = d_i / kBank;
     const int Tp = (int)((T + 63) / 64 * 64);
-    const BwdLayout L = layout(T, d, d_i, r);
+    const bool have_wt = a.W_gT != nullptr && a.W_uT != nullptr;
+    const BwdLayout L = layout(T, d, d_i, r, have_wt);
     void* ws = a.ws;
     uint16_t* z16 = at<uint16_t>(ws, L.z16);
     float* p32 = at<float>(ws, L.p32);
@@ -230,8 +236,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     uint16_t* gzT = at<uint16_t>(ws, L.gzT);
     uint16_t* BT = at<uint16_t>(ws, L.BT);
     uint16_t* AT = at<uint16_t>(ws, L.AT);
-    uint16_t* WgT = at<uint16_t>(ws, L.WgT);
-    uint16_t* WuT = at<uint16_t>(ws, L.WuT);
+    const uint16_t* WgT = have_wt ? a.W_gT : at<uint16_t>(ws, L.WgT);
+    const uint16_t* WuT = have_wt ? a.W_uT : at<uint16_t>(ws, L.WuT);
     hipError_t e = hipSuccess;
     auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; return e == hipSuccess; };
 
@@ -264,8 +270,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     ok(launch_gemm_nt(gzT, XT, r, d, Tp, a.g_A, GemmOut::F32, s, nullptr, U32));
     // g_x = g_z A + g_u W_g + g_v W_u
     ok(launch_transpose(Dt::BF16, a.A, AT, r, d, s));
-    ok(launch_transpose(Dt::BF16, a.W_g, WgT, d_i, d, s));
-    ok(launch_transpose(Dt::BF16, a.W_u, WuT, d_i, d, s));
+    if (!have_wt) {
+        ok(launch_transpose(Dt::BF16, a.W_g, at<uint16_t>(ws, L.WgT), d_i, d, s));
+        ok(launch_transpose(Dt::BF16, a.W_u, at<uint16_t>(ws, L.WuT), d_i, d, s));
+    }
     ok(launch_gemm_nt(gz16, AT, T, d, r, a.g_x, GemmOut::F32, s, nullptr, U32));
     ok(launch_gemm_nt(gu16, WgT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, U32));
     ok(launch_gemm_nt(gv16, WuT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, U32));

@@ -64,11 +64,12 @@ sffn_status_t check_config(const sffn_config_t* c) {
         return fail(SFFN_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
     if (c->gate != SFFN_GATE_PREDICTOR && c->gate != SFFN_GATE_SILU && c->gate != SFFN_GATE_AMPLITUDE)
         return fail(SFFN_ERR_INVALID_ARG, "unknown gate %d", (int)c->gate);
+    if (c->flags & ~SFFN_FLAG_BACKWARD) return fail(SFFN_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return SFFN_OK;
 }
 
 struct PackedLayout {
-    size_t A, B, Wg, Wu, Wd, WdT, bias, total;
+    size_t A, B, Wg, Wu, Wd, WdT, bias, WgT, WuT, total;   // WgT, WuT: SFFN_FLAG_BACKWARD only
 };
 
 PackedLayout packed_layout(const sffn_config_t& c) {
@@ -83,6 +84,11 @@ PackedLayout packed_layout(const sffn_config_t& c) {
     L.Wd = off;   off += align_up(d * di * e);
     L.WdT = off;  off += align_up(di * d * e);
     L.bias = off; off += align_up(di * 4);
+    L.WgT = L.WuT = 0;
+    if (c.flags & SFFN_FLAG_BACKWARD) {
+        L.WgT = off; off += align_up(d * di * e);
+        L.WuT = off; off += align_up(d * di * e);
+    }
     L.total = off;
     return L;
 }
@@ -210,6 +216,10 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* w_gate, co
     cp(L.Wd, w_down, d * di * e);
     if (pred_bias) cp(L.bias, pred_bias, di * 4);
     if (he == hipSuccess) he = sffn::launch_transpose(dt, w_down, at<char>(packed, L.WdT), cfg->d, cfg->d_i, s);
+    if (cfg->flags & SFFN_FLAG_BACKWARD) {
+        if (he == hipSuccess) he = sffn::launch_transpose(dt, w_gate, at<char>(packed, L.WgT), cfg->d_i, cfg->d, s);
+        if (he == hipSuccess) he = sffn::launch_transpose(dt, w_up, at<char>(packed, L.WuT), cfg->d_i, cfg->d, s);
+    }
     if (he == hipSuccess) he = hipStreamSynchronize(s);
     if (he != hipSuccess) return hip_status(he, "sparse_ffn_create");
 
@@ -317,7 +327,8 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
 
 size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T) {
     if (!h || T <= 0) return 0;
-    return sffn::backward_workspace_bytes(T, h->cfg.d, h->cfg.d_i, h->cfg.rank);
+    return sffn::backward_workspace_bytes(T, h->cfg.d, h->cfg.d_i, h->cfg.rank,
+                                          (h->cfg.flags & SFFN_FLAG_BACKWARD) != 0);
 }
 
 sffn_status_t sparse_ffn_backward(sffn_handle_t h, const void* x, const void* g_y, const uint64_t* mask,
@@ -375,6 +386,10 @@ sffn_status_t sparse_ffn_backward(sffn_handle_t h, const void* x, const void* g_
     a.bias = h->has_bias ? at<const float>(pk, L.bias) : nullptr;
     a.W_g = at<const uint16_t>(pk, L.Wg); a.W_u = at<const uint16_t>(pk, L.Wu);
     a.W_dT = at<const uint16_t>(pk, L.WdT);
+    if (c.flags & SFFN_FLAG_BACKWARD) {
+        a.W_gT = at<const uint16_t>(pk, L.WgT);
+        a.W_uT = at<const uint16_t>(pk, L.WuT);
+    }
     a.g_x = g_x; a.g_A = g_A; a.g_B = g_B; a.g_Wg = g_Wg; a.g_Wu = g_Wu; a.g_Wd = g_Wd;
     a.g_bias = h->has_bias ? g_bias : nullptr;
     a.ws = workspace;

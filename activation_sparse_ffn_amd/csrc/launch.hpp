@@ -166,10 +166,13 @@ struct BwdArgs {
     const uint16_t* W_g;            // [d_i, d]
     const uint16_t* W_u;            // [d_i, d]
     const uint16_t* W_dT;           // [d_i, d]
+    const uint16_t* W_gT;           // [d, d_i] or null (then transposed into the workspace)
+    const uint16_t* W_uT;           // [d, d_i] or null
     float *g_x, *g_A, *g_B, *g_bias, *g_Wg, *g_Wu, *g_Wd;   // outputs (g_bias may be null)
     void* ws;                       // workspace of backward_workspace_bytes(...)
 };
-size_t backward_workspace_bytes(int64_t T, int d, int d_i, int rank);
+// weights_t: W_g^T and W_u^T come with the layer (no room for them needed)
+size_t backward_workspace_bytes(int64_t T, int d, int d_i, int rank, bool weights_t);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 // x[0 .. n) = 0
 hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t s);

@@ -253,8 +253,9 @@ def backward_bench(args):
     ffns = []
     for li in range(n_layers):
         L = wl.make_layer(shape, seed=li)
+        # a layer meant for training keeps W_g^T and W_u^T packed
         ffns.append(sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B), None,
-                                   keep=args.keep, gate=args.gate))
+                                   keep=args.keep, gate=args.gate, for_backward=True))
         del L
     x = dev(wl.make_tokens(shape, T, seed=1, outlier_frac=0.01))
     gy = dev(wl.make_tokens(shape, T, seed=2))

@@ -78,6 +78,14 @@ typedef enum {
  * keep = 16 (Methodologie > 1. Architectuur); d is the model width.
  * Requirements: bank == 64; 1 <= keep <= 64; d_i % 64 == 0 and
  * d_i <= 65536; d % 64 == 0; rank % 32 == 0; all positive. */
+/* Options of a layer (bits of sffn_config_t.flags). */
+typedef enum {
+    /* The packed buffer also holds W_g^T and W_u^T ([d, d_i] each, 4 d d_i
+     * more bytes for bf16), so that sparse_ffn_backward does not transpose
+     * them on every call. */
+    SFFN_FLAG_BACKWARD = 1
+} sffn_flag_t;
+
 typedef struct {
     int32_t d;
     int32_t d_i;
@@ -86,6 +94,7 @@ typedef struct {
     int32_t keep;
     sffn_dtype_t dtype;   /* element type of x, y and every weight */
     sffn_gate_t gate;
+    int32_t flags;        /* SFFN_FLAG_* bits; 0 for none */
 } sffn_config_t;
 
 typedef struct sffn_layer* sffn_handle_t;
@@ -167,7 +176,8 @@ const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i);
 
 /* Workspace bytes sparse_ffn_backward needs for T tokens (0 for T <= 0 or
  * a null handle). About 10 fp32/bf16 [T, d_i] buffers plus the transposed
- * weights: ~2.4 GB at T = 4096, d = 4096, d_i = 14336. */
+ * weights (W_g^T and W_u^T only without SFFN_FLAG_BACKWARD): ~2.4 GB at
+ * T = 4096, d = 4096, d_i = 14336. */
 size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T);
 
 /* Backward pass of a forward of T tokens ("Continual LLM Upcycling",

@@ -60,9 +60,13 @@ def test_packed_size_and_config_checks(lib):
     assert size >= e * (r * d + di * r + 4 * di * d) + 4 * di
     assert size < e * (r * d + di * r + 4 * di * d) + 4 * di + 8 * 256
     for bad in (dict(bank=32), dict(keep=0), dict(keep=65), dict(d_i=1000), dict(d=100),
-                dict(rank=40), dict(d=0), dict(dtype=7), dict(gate=3), dict(d_i=65536 + 64)):
+                dict(rank=40), dict(d=0), dict(dtype=7), dict(gate=3), dict(d_i=65536 + 64),
+                dict(flags=2), dict(flags=-1)):
         assert lib.sparse_ffn_packed_size(ctypes.byref(_cfg(**bad))) == 0, bad
     assert lib.sparse_ffn_packed_size(None) == 0
+    # SFFN_FLAG_BACKWARD adds W_g^T and W_u^T (bf16, [d, d_i] each)
+    with_t = lib.sparse_ffn_packed_size(ctypes.byref(_cfg(flags=sffn.SFFN_FLAG_BACKWARD)))
+    assert with_t == size + 2 * e * d * di
 
 
 def test_bank_topk_rejections(lib):

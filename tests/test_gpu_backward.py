@@ -80,3 +80,26 @@ def full_layer():
 @pytest.mark.parametrize("T,gate", [(64, "pred"), (300, "silu")])
 def test_backward_full(full_layer, T, gate):
     run_and_check(full_layer, T, gate, 16, 1.0, seed=900 + T)
+
+
+@pytest.mark.parametrize("T", [70, 300])
+def test_backward_with_packed_weight_transposes(mid_layer, T):
+    """A layer created for the backward (W_g^T and W_u^T packed once) gives
+    the same gradients bit for bit, from a smaller workspace."""
+    import activation_sparse_ffn_amd as sffn
+    x = dev(wl.make_tokens(MID, T, seed=41))
+    gy = dev(wl.make_tokens(MID, T, seed=42))
+    plain = make_ffn(mid_layer, bias=True)
+    L = mid_layer
+    ready = sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B), dev(L.bias),
+                           for_backward=True)
+    assert ready.packed.numel() == plain.packed.numel() + 4 * MID.d * MID.d_i
+    _, mask = plain(x, return_mask=True)
+    g0 = plain.backward(x, gy, mask)
+    g1 = ready.backward(x, gy, mask)
+    torch.cuda.synchronize()
+    for name in ("x", "A", "B", "bias", "W_g", "W_u", "W_d"):
+        assert torch.equal(g0[name], g1[name]), name
+    lib = sffn.load_library()
+    assert lib.sparse_ffn_backward_workspace_size(ready._h, T) \
+        == lib.sparse_ffn_backward_workspace_size(plain._h, T) - 4 * MID.d * MID.d_i
