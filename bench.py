@@ -295,9 +295,9 @@ def backward_bench(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the layer would shard by tokens or by banks; see the design notes).",
-              file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the layer would shard by tokens, with no exchange, or by banks, with one "
+              "all-reduce of y).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

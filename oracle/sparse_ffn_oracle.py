@@ -22,7 +22,7 @@ Sparsity Training Recipe for Dense-to-Sparse LLMs":
 * same summary, 3. Hardware Implicaties: inactive channels may skip all three
   projections (gate, up, down).
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * predictor: linear low-rank factorisation p = (x A^T) B^T (+ bias), no
   nonlinearity between the two layers;
@@ -40,8 +40,8 @@ Readings where the pages are silent (each one is listed in the design doc):
 The backward pass follows the same summary's Executie > Backward Pass: the
 non-differentiable top-k is crossed by a soft, sigmoid-like local gradient
 around the selection threshold, so the language-modelling loss reaches the
-predictor. Its form is not given; the reading taken here (listed in
-the design doc): the forward keeps the hard mask m; the backward differentiates
+predictor. Its form is not given; the reading taken here: the forward keeps
+the hard mask m; the backward differentiates
 m as if it were sigmoid((p - theta) / tau), with theta the midpoint of the
 bank's keep-th and (keep+1)-th largest logits (held constant) and tau > 0 the
 caller's temperature; the mask's gradient g_h * s * u * v is taken for every
