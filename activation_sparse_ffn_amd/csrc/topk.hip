@@ -3,6 +3,9 @@
 // (gist.science technical summary, Methodologie > 1. Architectuur): the
 // intermediate width is split into fixed banks of 64 channels and a hard
 // top-k keeps `keep` channels of each bank.
+#include <algorithm>
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,76 +50,148 @@ __global__ __launch_bounds__(256) void k_bank_topk(const float* __restrict__ log
     }
 }
 
-// Many banks: one bank per lane. A wave stages the logits of 64 consecutive
-// (token, bank) words (16 KB, read with whole-line loads) in wave-private LDS,
-// 16-byte chunks XOR-swizzled by bank so that each lane can read its own bank
-// without bank conflicts. Each lane sorts its 64 order-preserving keys with a
-// bitonic network held in registers (max/min pairs, no branches), takes the
-// keep-th largest key as the threshold, and rebuilds the mask in channel
-// order: keys above the threshold are kept, keys equal to it are kept lowest
-// channel first until `keep` are taken -- the same rule as wave_bank_topk.
-__global__ __launch_bounds__(256) void k_bank_topk_lanes(const float* __restrict__ logits,
-                                                         int64_t n_words, int keep,
-                                                         uint64_t* __restrict__ mask,
-                                                         uint16_t* __restrict__ ids, int nb,
-                                                         uint16_t* __restrict__ gate,
-                                                         int gate_mode) {
-    __shared__ __attribute__((aligned(16))) float stage[4][kWave * kBank];
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t w0 = ((int64_t)blockIdx.x * 4 + wv) * kWave;      // first word of this wave
-    float* st = stage[wv];
-    char* stb = reinterpret_cast<char*>(st);
-
-    // coalesced fetch: instruction q, lane l -> word q * 4 + l / 16, chunk l % 16
+// Many banks: one bank per lane. Each wave is a workgroup of its own and
+// walks chunks of 64 consecutive (token, bank) words (16 KB), chunk c, c +
+// n_waves, ...: a chunk's logits go from global memory straight into the
+// wave's 16 KB LDS buffer (buffer loads to LDS, non-temporal, whole-line
+// reads; 16-byte pieces XOR-swizzled by bank so that each lane reads its
+// own bank without LDS bank conflicts). The wave copies its chunk into
+// registers, starts the next chunk's loads into the freed buffer at once,
+// and ranks from registers while they are in flight; with two such waves
+// per SIMD the loads of one overlap the ranking of the other as well. Each
+// lane sorts its 64 order-preserving keys with sorting networks held in
+// registers (max/min pairs, no branches), takes the keep-th largest key as
+// the threshold, and rebuilds the mask in channel order: keys above the
+// threshold are kept, keys equal to it are kept lowest channel first until
+// `keep` are taken -- the same rule as wave_bank_topk.
+typedef float f4v __attribute__((ext_vector_type(4)));
+// Sixteen 16-byte LDS reads, complete when the block ends. Written as one
+// asm block so that the compiler's conservative wait before LDS reads that
+// follow LDS-bound loads does not stall on the next chunk's loads; the
+// caller orders the reads after an explicit wait for the chunk.
+__device__ __forceinline__ void lds_read16(const uint32_t (&a)[16], f4v (&v)[16]) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\tds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %20\n\tds_read_b128 %5, %21\n\tds_read_b128 %6, %22\n\tds_read_b128 %7, %23\n\t"
+        "ds_read_b128 %8, %24\n\tds_read_b128 %9, %25\n\tds_read_b128 %10, %26\n\tds_read_b128 %11, %27\n\t"
+        "ds_read_b128 %12, %28\n\tds_read_b128 %13, %29\n\tds_read_b128 %14, %30\n\tds_read_b128 %15, %31\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
+        : "memory");
+}
+// The lane's whole 256-byte word, piece c in v[c]; `key` is the word's LDS
+// address with the lane's swizzle (bank % 16) * 16 or-ed in.
+__device__ __forceinline__ void read_word(uint32_t key, f4v (&v)[16]) {
+    asm volatile("" : "+v"(key));  // keep the 16 addresses out of the loop's live set
+    uint32_t a[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int L = q * 4 + (lane >> 4), c = lane & 15;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (w0 + L < n_words) val = *reinterpret_cast<const float4*>(logits + (w0 + L) * kBank + 4 * c);
-        *reinterpret_cast<float4*>(stb + L * 256 + ((c ^ (L & 15)) << 4)) = val;
-    }
-    const int64_t gw = w0 + lane;                  // this lane's word
-    const bool live = gw < n_words;
-
-    const uint64_t sel = lane_select64(
-        [stb, lane](int c) { return *reinterpret_cast<const float4*>(stb + lane * 256 + ((c ^ (lane & 15)) << 4)); },
-        keep);
-    if (!live) return;
-    mask[gw] = sel;
-    const unsigned t = (unsigned)gw / (unsigned)nb;
-    const unsigned b = (unsigned)gw - t * (unsigned)nb;
-    if (ids != nullptr) {
-        int slot = 0;
+    for (int c = 0; c < 16; ++c) a[c] = key ^ (uint32_t)(c << 4);
+    lds_read16(a, v);
+}
+// The 16 loads of one chunk, instruction Q = 4 a + r. The immediate offset
+// moves both the source and the LDS destination, so the LDS base steps by
+// 4096 only. Full chunks take the 4096 a part as the scalar offset; the
+// last, partial chunk puts it in the lane offset, where the range check of
+// the resource sees it, and its loads past the logits' end read zeros.
+template <int... Q>
+__device__ __forceinline__ void chunk_loads(__amdgpu_buffer_rsrc_t rs, __attribute__((address_space(3))) char* d3,
+                                            const uint32_t (&voff)[4], bool full, std::integer_sequence<int, Q...>) {
+    constexpr int kNonTemporal = 2;
+    if (full)
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d3 + 4096 * (Q >> 2), 16, voff[Q & 3], 4096 * (Q >> 2),
+                                                  1024 * (Q & 3), kNonTemporal),
+         ...);
+    else
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d3 + 4096 * (Q >> 2), 16, voff[Q & 3] + 4096 * (Q >> 2), 0,
+                                                  1024 * (Q & 3), kNonTemporal),
+         ...);
+}
+constexpr uint32_t kRawBufferWord3 = 0x00020000;  // 32-bit data format, untyped byte-addressed access
+constexpr int kTopkLanesWaves = 8;  // two waves per SIMD: <= 256 registers and 16 KB of LDS each
+__global__ __launch_bounds__(64) void k_bank_topk_lanes(const float* __restrict__ logits,
+                                                        int64_t n_words, int keep,
+                                                        uint64_t* __restrict__ mask,
+                                                        uint16_t* __restrict__ ids, int nb,
+                                                        uint16_t* __restrict__ gate,
+                                                        int gate_mode) {
+    __shared__ __attribute__((aligned(16))) char st0[kWave * kBank * 4];
+    const int lane = threadIdx.x;
+    const int64_t n_chunks = (n_words + kWave - 1) / kWave;
+    const int64_t stride = gridDim.x;
+    // Instruction q (q = 4 a + r) fills bytes [1024 q, 1024 q + 1024) of the
+    // buffer: lane l lands in word L = 4 q + l / 16, slot l % 16, which holds
+    // chunk (l % 16) ^ (L % 16) of that word. L % 16 = 4 r + l / 16, so the
+    // lane's source offset is 4096 a + 1024 r + voff[r].
+    uint32_t voff[4];
 #pragma unroll
-        for (int i = 0; i < kBank; ++i)
-            if ((sel >> i) & 1ull) ids[gw * keep + slot++] = (uint16_t)(b * kBank + i);
-    }
-    if (gate != nullptr) {
-        const unsigned col_tiles = (unsigned)nb * kBank / kGateTileCols;
-        const unsigned j0 = b * kBank;
-        uint16_t* gp = gate + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
-                                  (kGateTileRows * kGateTileCols) +
-                       (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
+    for (int r = 0; r < 4; ++r)
+        voff[r] = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ (4 * r + (lane >> 4))));
+    auto fetch = [&](int64_t ch, char* dst) {
+        const int64_t w0 = ch * kWave;
+        const int64_t left = n_words - w0;
+        void* base = (void*)(logits + w0 * kBank);
+        auto* d3 = (__attribute__((address_space(3))) char*)dst;
+        const bool full = left >= kWave;
+        const int nbytes = full ? kWave * kBank * 4 : (int)left * kBank * 4;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nbytes, kRawBufferWord3);
+        chunk_loads(rs, d3, voff, full, std::make_integer_sequence<int, 16>{});
+    };
+    auto rank = [&](int64_t ch, const char* stb) {
+        const int64_t gw = ch * kWave + lane;              // this lane's word
+        const uint32_t key = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)stb + lane * 256 +
+                             ((lane & 15) << 4);
+        f4v buf[16];
+        read_word(key, buf);
+        if (ch + stride < n_chunks) fetch(ch + stride, st0);   // the buffer is free again
+        const uint64_t sel = lane_select64(
+            [&](int c) { return make_float4(buf[c].x, buf[c].y, buf[c].z, buf[c].w); }, keep);
+        if (gw >= n_words) return;
+        mask[gw] = sel;
+        const unsigned t = (unsigned)gw / (unsigned)nb;
+        const unsigned b = (unsigned)gw - t * (unsigned)nb;
+        if (ids != nullptr) {
+            int slot = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float4 v0 = *reinterpret_cast<const float4*>(stb + lane * 256 + (((2 * c) ^ (lane & 15)) << 4));
-            const float4 v1 = *reinterpret_cast<const float4*>(stb + lane * 256 + (((2 * c + 1) ^ (lane & 15)) << 4));
-            const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint32_t hw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint16_t h2[2];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int i = 8 * c + 2 * e + q;
-                    const float g = gate_mode ? 1.f : sigmoidf_dev(pv[2 * e + q]);
-                    h2[q] = ((sel >> i) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)g) : kGateDropped;
-                }
-                hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
-            }
-            *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            for (int i = 0; i < kBank; ++i)
+                if ((sel >> i) & 1ull) ids[gw * keep + slot++] = (uint16_t)(b * kBank + i);
         }
+        if (gate != nullptr) {
+            const unsigned col_tiles = (unsigned)nb * kBank / kGateTileCols;
+            const unsigned j0 = b * kBank;
+            uint16_t* gp = gate + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
+                                      (kGateTileRows * kGateTileCols) +
+                           (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const f4v v0 = buf[2 * c], v1 = buf[2 * c + 1];
+                const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint16_t h2[2];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int i = 8 * c + 2 * e + q;
+                        const float g = gate_mode ? 1.f : sigmoidf_dev(pv[2 * e + q]);
+                        h2[q] = ((sel >> i) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)g) : kGateDropped;
+                    }
+                    hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+                }
+                *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            }
+        }
+    };
+    // One wave per workgroup: the reads of a chunk complete inside
+    // read_word, before the loads that overwrite the buffer are issued;
+    // s_waitcnt(0) makes the chunk's loads (and the previous chunk's stores)
+    // complete before it is read.
+    if ((int64_t)blockIdx.x < n_chunks) fetch(blockIdx.x, st0);
+    for (int64_t ch = blockIdx.x; ch < n_chunks; ch += stride) {
+        __builtin_amdgcn_s_waitcnt(0);
+        rank(ch, st0);
     }
 }
 
@@ -141,8 +216,13 @@ hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
     const int nb = d_i / kBank;
     const int64_t n_words = T * nb;
     if (n_words >= 65536) {
-        const int64_t blocks = (n_words + 4 * kWave - 1) / (4 * kWave);
-        xlaunch(events, stage, k_bank_topk_lanes, dim3((unsigned)blocks), dim3(256), 0, s, logits,
+        int dev = 0, n_cu = 0;
+        (void)hipGetDevice(&dev);
+        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+            n_cu = 256;
+        const int64_t chunks = (n_words + kWave - 1) / kWave;
+        const int64_t waves = std::min<int64_t>(chunks, (int64_t)n_cu * kTopkLanesWaves);
+        xlaunch(events, stage, k_bank_topk_lanes, dim3((unsigned)waves), dim3(kWave), 0, s, logits,
                 n_words, keep, mask, ids, nb, gate_tiles, gate_mode);
     } else {
         const int64_t blocks = (n_words + 3) / 4;
