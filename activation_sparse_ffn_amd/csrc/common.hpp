@@ -108,6 +108,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 // a = -inf gives rcp(inf) = 0, a = +inf gives 1, NaN stays NaN.
 __device__ __forceinline__ float sigmoidf_dev(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
+// Sum of `splits` K-split partials p[0], p[n], p[2 n], ... in that order.
+// The loads of a group of 8 are all issued before its first add, so a
+// thread waits for memory once per group instead of once per split.
+__device__ __forceinline__ float sum_splits_in_order(const float* __restrict__ p, int splits, int64_t n) {
+    constexpr int G = 8;
+    float acc = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += G) {
+        float v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) v[k] = s0 + k < splits ? p[(size_t)(s0 + k) * n] : 0.f;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (s0 + k < splits) acc += v[k];
+    }
+    return acc;
+}
+
 // Order-preserving 32-bit key of a logit: larger value <=> larger key.
 // -0 and +0 share a key; every NaN gets key 0, below -inf (0x007fffff).
 __device__ __forceinline__ uint32_t rank_key(float f) {

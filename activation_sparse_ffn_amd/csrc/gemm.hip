@@ -712,8 +712,7 @@ __global__ __launch_bounds__(256) void k_sum_splits_bf16(const float* __restrict
                                                          int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
-    float acc = 0.f;
-    for (int k = 0; k < splits; ++k) acc += partial[(size_t)k * n + i];
+    const float acc = sum_splits_in_order(partial + i, splits, n);
     C[i] = f32_to_bf16(acc);
 }
 
@@ -831,8 +830,7 @@ __global__ __launch_bounds__(256) void k_sum_splits_out(const float* __restrict_
                                                         const float* __restrict__ bias) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
-    float acc = 0.f;
-    for (int k = 0; k < splits; ++k) acc += partial[(size_t)k * n + i];
+    float acc = sum_splits_in_order(partial + i, splits, n);
     if (bias) acc += bias[i % N];
     if (mode == 2) static_cast<uint16_t*>(C)[i] = f32_to_bf16(acc);
     else if (mode == 1) static_cast<float*>(C)[i] += acc;

@@ -219,8 +219,7 @@ __global__ __launch_bounds__(256) void k_skinny_sum_bf16(const float* __restrict
                                                          int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) acc += partial[(size_t)s * n + i];
+    const float acc = sum_splits_in_order(partial + i, splits, n);
     C[i] = f32_to_bf16(acc);
 }
 
