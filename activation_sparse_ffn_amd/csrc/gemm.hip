@@ -787,8 +787,8 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     } else {
         g.A = a.z; g.B0 = a.B; g.M = a.T; g.N = a.d_i; g.K = a.rank; g.Cf = a.logits; g.bias = a.bias;
         gemm<EPI_F32_BIAS>(g, s, a.events, 1);
-        hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2,
-                                        tiles ? a.gate_tiles : nullptr, a.gate);
+        // (gate tiles imply the fused branch above, so none are written here)
+        hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2);
         if (e != hipSuccess) return e;
     }
     // H = select(m, s u v, 0)

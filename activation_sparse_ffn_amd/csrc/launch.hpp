@@ -46,17 +46,19 @@ inline void xlaunch(void* const* events, int stage, F kernel, dim3 grid, dim3 bl
     hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, args...);
 }
 
-// ---- bank top-k (one wave per (token, bank)) ------------------------------
-// Optional gate output for the 256 x 128 gate/up GEMM tiles (d_i % 128 == 0):
-// fp16 bits, tile-contiguous, G[t / 256][j / 128][t % 256][j % 128] =
-// sigmoid(p) (predictor gate) or 1 (silu gate) for kept channels, -1 for
-// dropped ones. Rows t >= T of the last tile are not written.
+// ---- gate tiles ------------------------------------------------------------
+// Gate input of the 256 x 128 gate/up GEMM tiles (d_i % 128 == 0), written by
+// the fused predictor-layer-2 + top-k GEMM: fp16 bits, tile-contiguous,
+// G[t / 256][j / 128][t % 256][j % 128] = sigmoid(p) (predictor gate) or 1
+// (silu gate) for kept channels, -1 for dropped ones. Rows t >= T of the last
+// tile are not written.
 constexpr int kGateTileRows = 256, kGateTileCols = 128;
 constexpr uint16_t kGateDropped = 0xbc00;   // fp16 -1.0
+
+// ---- bank top-k of fp32 logits [T, d_i]: mask words, optional kept ids ------
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s,
-                            void* const* events = nullptr, int stage = 0,
-                            uint16_t* gate_tiles = nullptr, int gate_mode = 0);
+                            void* const* events = nullptr, int stage = 0);
 
 // ---- token-gather path (VALU; decode and fp32 layers) ---------------------
 struct GatherArgs {

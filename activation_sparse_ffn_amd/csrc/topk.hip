@@ -18,8 +18,7 @@ template <int BPW>
 __global__ __launch_bounds__(256) void k_bank_topk(const float* __restrict__ logits,
                                                    int64_t n_words, int keep,
                                                    uint64_t* __restrict__ mask,
-                                                   uint16_t* __restrict__ ids, int nb,
-                                                   uint16_t* __restrict__ gate, int gate_mode) {
+                                                   uint16_t* __restrict__ ids, int nb) {
     const int lane = threadIdx.x & 63;
     const int64_t w0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * BPW;
     float v[BPW];
@@ -36,16 +35,6 @@ __global__ __launch_bounds__(256) void k_bank_topk(const float* __restrict__ log
         if (ids != nullptr && kept) {
             const int b = (int)(gb % nb);
             ids[gb * keep + lanes_below(sel)] = (uint16_t)(b * kBank + lane);
-        }
-        if (gate != nullptr) {
-            const unsigned t = (unsigned)gb / (unsigned)nb;
-            const unsigned j = ((unsigned)gb - t * (unsigned)nb) * kBank + lane;
-            const unsigned col_tiles = (unsigned)nb * kBank / kGateTileCols;
-            const size_t o = ((size_t)(t / kGateTileRows) * col_tiles + j / kGateTileCols) *
-                                 (kGateTileRows * kGateTileCols) +
-                             (t % kGateTileRows) * kGateTileCols + j % kGateTileCols;
-            const float g = gate_mode ? 1.f : sigmoidf_dev(v[i]);
-            gate[o] = kept ? __builtin_bit_cast(uint16_t, (_Float16)g) : kGateDropped;
         }
     }
 }
@@ -114,9 +103,7 @@ constexpr int kTopkLanesWaves = 8;  // two waves per SIMD: <= 256 registers and 
 __global__ __launch_bounds__(64) void k_bank_topk_lanes(const float* __restrict__ logits,
                                                         int64_t n_words, int keep,
                                                         uint64_t* __restrict__ mask,
-                                                        uint16_t* __restrict__ ids, int nb,
-                                                        uint16_t* __restrict__ gate,
-                                                        int gate_mode) {
+                                                        uint16_t* __restrict__ ids, int nb) {
     __shared__ __attribute__((aligned(16))) char st0[kWave * kBank * 4];
     const int lane = threadIdx.x;
     const int64_t n_chunks = (n_words + kWave - 1) / kWave;
@@ -150,38 +137,12 @@ __global__ __launch_bounds__(64) void k_bank_topk_lanes(const float* __restrict_
             [&](int c) { return make_float4(buf[c].x, buf[c].y, buf[c].z, buf[c].w); }, keep);
         if (gw >= n_words) return;
         mask[gw] = sel;
-        const unsigned t = (unsigned)gw / (unsigned)nb;
-        const unsigned b = (unsigned)gw - t * (unsigned)nb;
         if (ids != nullptr) {
+            const int b = (int)(gw % nb);
             int slot = 0;
 #pragma unroll
             for (int i = 0; i < kBank; ++i)
                 if ((sel >> i) & 1ull) ids[gw * keep + slot++] = (uint16_t)(b * kBank + i);
-        }
-        if (gate != nullptr) {
-            const unsigned col_tiles = (unsigned)nb * kBank / kGateTileCols;
-            const unsigned j0 = b * kBank;
-            uint16_t* gp = gate + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
-                                      (kGateTileRows * kGateTileCols) +
-                           (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const f4v v0 = buf[2 * c], v1 = buf[2 * c + 1];
-                const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                uint32_t hw[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint16_t h2[2];
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int i = 8 * c + 2 * e + q;
-                        const float g = gate_mode ? 1.f : sigmoidf_dev(pv[2 * e + q]);
-                        h2[q] = ((sel >> i) & 1ull) ? __builtin_bit_cast(uint16_t, (_Float16)g) : kGateDropped;
-                    }
-                    hw[e] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
-                }
-                *reinterpret_cast<uint4*>(gp + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            }
         }
     };
     // One wave per workgroup: the reads of a chunk complete inside
@@ -212,7 +173,7 @@ size_t gate_tiles_bytes(int64_t T, int d_i) {
 
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s, void* const* events,
-                            int stage, uint16_t* gate_tiles, int gate_mode) {
+                            int stage) {
     const int nb = d_i / kBank;
     const int64_t n_words = T * nb;
     if (n_words >= 65536) {
@@ -223,11 +184,11 @@ hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
         const int64_t chunks = (n_words + kWave - 1) / kWave;
         const int64_t waves = std::min<int64_t>(chunks, (int64_t)n_cu * kTopkLanesWaves);
         xlaunch(events, stage, k_bank_topk_lanes, dim3((unsigned)waves), dim3(kWave), 0, s, logits,
-                n_words, keep, mask, ids, nb, gate_tiles, gate_mode);
+                n_words, keep, mask, ids, nb);
     } else {
         const int64_t blocks = (n_words + 3) / 4;
         xlaunch(events, stage, k_bank_topk<1>, dim3((unsigned)blocks), dim3(256), 0, s, logits,
-                n_words, keep, mask, ids, nb, gate_tiles, gate_mode);
+                n_words, keep, mask, ids, nb);
     }
     return hipGetLastError();
 }
