@@ -177,6 +177,24 @@ def test_bank_topk_many_banks_per_wave(keep):
     np.testing.assert_array_equal(ids_np, want)
 
 
+@pytest.mark.parametrize("T,keep", [(4096, 16), (16387, 16), (16387, 5)])
+def test_bank_topk_persistent_chunks(T, keep):
+    """The many-banks kernel at its lower size bound (4096 x 16 = 65536
+    words, whole 64-word chunks) and where each wave walks several chunks
+    and the last chunk is partial (16387 x 16 words = 4096 chunks + 48)."""
+    import activation_sparse_ffn_amd as sffn
+    p = wl.make_tie_logits(T=T, d_i=1024, seed=20 + keep)
+    p[::5] = np.random.default_rng(21).standard_normal((len(p[::5]), 1024)).astype(np.float32)
+    p[T - 1, 960:] = np.nan                   # the very last bank: NaNs only
+    p[T - 2, 0:64:2] = -np.inf
+    mask, ids = sffn.bank_topk(dev(p), keep=keep, return_ids=True)
+    torch.cuda.synchronize()
+    m = o.bank_topk_mask(p, 64, keep)
+    np.testing.assert_array_equal(words(mask), o.mask_to_words(m))
+    ids_np = ids.cpu().numpy().view(np.uint16).astype(np.int64)
+    np.testing.assert_array_equal(ids_np, np.nonzero(m)[1].reshape(len(p), -1))
+
+
 def test_bank_topk_stress_full_size():
     """32768 x 14336 fp32 logits with 5% exact ties per bank: the oracle on a
     seeded sample of tokens, structural properties on every bank."""
