@@ -2,7 +2,7 @@
 """Throughput of the predictor-gated bank-wise sparse SwiGLU FFN forward on
 one MI355X, with the CPU oracle timed beside it.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|batched|prefill]
+    python bench.py [--steps K] [--warmup W] [--workload decode|batched|prefill|long|...]
 
 A step is one whole forward of the layer (predictor, bank top-k, gate/up on
 kept rows, down on kept columns) over one batch of synthetic tokens already
@@ -16,6 +16,9 @@ resident in HBM:
            Infinity Cache. This is the default and the headline.
   batched  32 tokens per step, predictor output bias b ~ N(0, 0.5).
   prefill  4096 tokens per step with 1% outlier feature columns.
+  long     32768 tokens per step with the same outliers, run as 8 forwards of
+           4096-token chunks through one handle (stage times and the
+           roofline entry are per chunk).
   topk     the bank top-k alone over 32768 x 14336 fp32 logits with 5% exact
            ties per bank (mask output), as GB/s against HBM.
   copy     not the layer: a plain 1 GiB device-to-device copy, timed and
@@ -48,6 +51,8 @@ WORKLOADS = {
     "decode": dict(T=1, layers=32, bias=False, outliers=0.0),
     "batched": dict(T=32, layers=8, bias=True, outliers=0.0),
     "prefill": dict(T=4096, layers=2, bias=False, outliers=0.01),
+    # a 32768-token forward as 8 chunks of 4096 through one handle
+    "long": dict(T=32768, chunk=4096, layers=2, bias=False, outliers=0.01),
 }
 
 
@@ -62,6 +67,9 @@ def parse():
                     help="budget of the oracle's bounded CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="chunked workloads: streams the chunks alternate over (each with its "
+                         "own workspace), so that one chunk's kernels can fill another's gaps")
     ap.add_argument("--keep", type=int, default=16,
                     help="channels kept per 64-channel bank (64: the dense modes)")
     ap.add_argument("--gate", choices=["pred", "silu", "amplitude"], default="pred",
@@ -344,19 +352,38 @@ def main():
     xs = [dev(wl.make_tokens(shape, T, seed=10_000 + i, outlier_frac=cfg["outliers"]))
           for i in range(n_x)]
     ys = [torch.empty_like(x) for x in xs]
-    ws = torch.empty(ffns[0].workspace_size(T), dtype=torch.uint8, device="cuda")
+    chunk = cfg.get("chunk", T)
+    n_chunks = T // chunk
+    n_streams = max(1, min(args.streams, n_chunks))
+    wss = [torch.empty(ffns[0].workspace_size(chunk), dtype=torch.uint8, device="cuda")
+           for _ in range(n_streams)]
     masks = [torch.empty((T, shape.n_banks), dtype=torch.int64, device="cuda") for _ in range(n_x)]
-    log(f"setup {time.time() - t0:.1f}s: {n_layers} layers, {n_x} token batches of T={T}")
+    log(f"setup {time.time() - t0:.1f}s: {n_layers} layers, {n_x} token batches of T={T}"
+        + (f" in {n_chunks} chunks of {chunk} over {n_streams} stream(s)" if n_chunks > 1 else ""))
 
     G = n_x * n_layers // np.gcd(n_x, n_layers)     # steps per graph: every (x, layer) pair once
     G = min(G, 64)
 
-    def step(i):
-        j = i % n_x
-        ffns[i % n_layers](xs[j], y=ys[j], mask=masks[j], workspace=ws)
-
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
+    side = [stream] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+
+    def step(i, streams=None):
+        j = i % n_x
+        f = ffns[i % n_layers]
+        if n_chunks == 1:
+            f(xs[j], y=ys[j], mask=masks[j], workspace=wss[0])
+            return
+        streams = streams or side
+        for s_ in streams[1:]:
+            s_.wait_stream(stream)
+        for c in range(n_chunks):
+            k = c % len(streams)
+            sl = slice(c * chunk, (c + 1) * chunk)
+            with torch.cuda.stream(streams[k]):
+                f(xs[j][sl], y=ys[j][sl], mask=masks[j][sl], workspace=wss[k])
+        for s_ in streams[1:]:
+            stream.wait_stream(s_)
     with torch.cuda.stream(stream):
         for i in range(W):
             step(i)
@@ -405,6 +432,10 @@ def main():
             fr.append(np.bitwise_count(np.bitwise_or.reduce(w, axis=0)).sum() / shape.d_i)
         union_frac = float(np.mean(fr))
     alg = algorithmic(args.workload, shape, T, union_frac, args.gate)
+    if n_chunks > 1:
+        # every chunk streams the weights of its own union again
+        for key in ("pred", "gateup", "down", "bytes"):
+            alg[key] *= n_chunks
 
     # ---- per-stage durations (kernel start/stop events) ---------------------
     n_ev = 2 * sffn.SFFN_STAGES
@@ -419,13 +450,13 @@ def main():
     n_prof = min(K, 256)
     with torch.cuda.stream(stream):
         for i in range(n_prof):
-            step(i)
+            step(i, streams=[stream])      # chunks in order: the events time the last one
             stream.synchronize()
             stage_ms += [evs[2 * s].elapsed_time(evs[2 * s + 1]) for s in range(sffn.SFFN_STAGES)]
     for f in ffns:
         f.set_stage_events(None)
     stage_us = stage_ms / n_prof * 1e3
-    names = ffns[0].stage_names(T)
+    names = ffns[0].stage_names(chunk)
     stages = {n: round(float(u), 3) for n, u in zip(names, stage_us) if n != "none"}
     log(f"stages (us): {stages}")
 
@@ -446,7 +477,7 @@ def main():
     else:
         dom = next(n for n in names if n.startswith("gateup"))
         dur_s = stage_us[names.index(dom)] * 1e-6
-        fl = 2 * T * 2 * shape.d_i * shape.d        # executed: dense gate and up
+        fl = 2 * chunk * 2 * shape.d_i * shape.d    # executed per launch: dense gate and up
         achieved = fl / dur_s / 1e12
         roof = dict(kernel="k_gemm<EPI_GATEUP>", bound="mfma", achieved=round(achieved, 1),
                     peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4),
@@ -476,6 +507,7 @@ def main():
             "workload": f"{args.workload}: {T} token(s) per step, d=4096, d_i=14336, rank=448, "
                         f"keep {args.keep} of 64 per bank, gate {args.gate}, {n_layers} layers rotated",
             "tokens_per_step": T, "layers_rotated": n_layers, "graph": graph is not None,
+            **({"chunk": chunk, "streams": n_streams} if n_chunks > 1 else {}),
         },
         "step_hbm_gbs": round(alg["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": alg["bytes"],
