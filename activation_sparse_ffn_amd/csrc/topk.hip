@@ -171,16 +171,28 @@ size_t gate_tiles_bytes(int64_t T, int d_i) {
     return (size_t)((T + kGateTileRows - 1) / kGateTileRows) * kGateTileRows * d_i * 2;
 }
 
+// Compute units of the current device, asked once per device (every thread
+// that races on the first call stores the same value).
+static int compute_units() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s, void* const* events,
                             int stage) {
     const int nb = d_i / kBank;
     const int64_t n_words = T * nb;
     if (n_words >= 65536) {
-        int dev = 0, n_cu = 0;
-        (void)hipGetDevice(&dev);
-        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-            n_cu = 256;
+        const int n_cu = compute_units();
         const int64_t chunks = (n_words + kWave - 1) / kWave;
         const int64_t waves = std::min<int64_t>(chunks, (int64_t)n_cu * kTopkLanesWaves);
         xlaunch(events, stage, k_bank_topk_lanes, dim3((unsigned)waves), dim3(kWave), 0, s, logits,
