@@ -158,9 +158,25 @@ def cpu_baseline(layer, T, budget_s, keep=16, gate="pred"):
         o.forward(x, layer.A, layer.B, layer.W_g, layer.W_u, layer.W_d, bias=layer.bias, keep=keep, gate=gate)
         n_tok += chunk
     el = time.perf_counter() - t0
-    return dict(value=n_tok / el, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"{n_tok} tokens of the same layer in groups of {chunk}, "
-                       f"{el:.1f} s wall, float64 numpy oracle")
+    out = dict(value=n_tok / el, unit="tokens/s", cores=int(cores), kind="oracle",
+               sample=f"{n_tok} tokens of the same layer in groups of {chunk}, "
+                      f"{el:.1f} s wall, float64 numpy oracle")
+    # the same on one thread, over a third of the budget
+    try:
+        from threadpoolctl import threadpool_limits
+        n1 = 0
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            while time.perf_counter() - t1 < budget_s / 3:
+                x = wl.make_tokens(layer.shape, chunk, seed=seed)
+                seed += 1
+                o.forward(x, layer.A, layer.B, layer.W_g, layer.W_u, layer.W_d, bias=layer.bias, keep=keep,
+                          gate=gate)
+                n1 += chunk
+            out["value_1_thread"] = n1 / (time.perf_counter() - t1)
+    except ImportError:
+        pass
+    return out
 
 
 def copy_calibration(args):
