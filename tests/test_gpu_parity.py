@@ -333,6 +333,20 @@ def test_forward_mid_shapes(mid_layer, T, gate):
     check_forward(mid_layer, x, y, mask, logits, bias=True, gate=gate)
 
 
+@pytest.mark.parametrize("keep", [4, 32])
+@pytest.mark.parametrize("T", [1, 5, 300])
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_forward_other_keep(mid_layer, keep, T, gate):
+    """keep other than 16 and 64 on every path: the generic gather kernels
+    (T = 1), the skinny MFMA path (T = 5) and the fused predictor-2 + top-k
+    GEMM, whose selection then takes the full 64-sort (T = 300)."""
+    ffn = make_ffn(mid_layer, bias=True, keep=keep, gate=gate)
+    x = wl.make_tokens(MID, T, seed=70 + T + keep)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(mid_layer, x, y, mask, logits, bias=True, keep=keep, gate=gate)
+
+
 @pytest.mark.parametrize("T", [2, 16])
 @pytest.mark.parametrize("gate", ["pred", "silu"])
 def test_keep_all_channels_is_dense(mid_layer, T, gate):
