@@ -156,8 +156,9 @@ def test_bank_topk_bit_exact(keep):
 
 @pytest.mark.parametrize("keep", [1, 16, 64])
 def test_bank_topk_many_banks_per_wave(keep):
-    """Above 65536 (token, bank) words each wave selects 8 banks; a ragged
-    tail (4099 x 16 words is not a multiple of 32) and ties included."""
+    """Above 65536 (token, bank) words each lane ranks one bank of a
+    64-word chunk; a ragged tail (4099 x 16 words is not a multiple of 64),
+    special values and ties included."""
     import activation_sparse_ffn_amd as sffn
     p = wl.make_tie_logits(T=4099, d_i=1024, seed=8)
     p[::7] = np.random.default_rng(3).standard_normal((len(p[::7]), 1024)).astype(np.float32)
@@ -235,9 +236,10 @@ def test_bank_topk_stress_full_size():
 # ---------------------------------------------------------------------------
 
 def test_forward_tiny_fp32():
+    """fp32 layers take the gather path at every T (here up to 257 tokens)."""
     layer = wl.make_layer(wl.TINY, seed=0)
     ffn = make_ffn(layer)
-    for T in (8, 1, 3):
+    for T in (8, 1, 3, 64, 257):
         x = wl.make_tokens(wl.TINY, T, seed=T)
         y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
         torch.cuda.synchronize()
