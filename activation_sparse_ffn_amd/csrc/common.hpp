@@ -225,6 +225,25 @@ __device__ __forceinline__ uint64_t lowest_bits(uint64_t x, int n) {
     return r;
 }
 
+// Bit i of the result is (v[i] >= t) (GE) or (v[i] > t) for i < 32, false
+// for NaN as in C. Each element costs one compare into VCC and one
+// add-with-carry that shifts the word left and brings the compare in, i.e.
+// acc = 2 acc + (compare); v[31] is taken first so that it ends in bit 31.
+template <bool GE>
+__device__ __forceinline__ uint32_t cmp_bits32(const float* v, float t) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 31; i >= 0; --i) {
+        if constexpr (GE)
+            asm("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+                : "+v"(acc) : "v"(v[i]), "v"(t) : "vcc");
+        else
+            asm("v_cmp_gt_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+                : "+v"(acc) : "v"(v[i]), "v"(t) : "vcc");
+    }
+    return acc;
+}
+
 // Keep mask of one 64-channel bank held entirely by one lane. `load(c)`
 // returns channels 4c .. 4c + 3 (c < 16) as a float4 and is called twice, so
 // the logits need not stay in registers across the selection.
@@ -284,23 +303,13 @@ __device__ __forceinline__ uint64_t lane_select64(Load load, int keep) {
         fv[4 * c + 2] = val.z;
         fv[4 * c + 3] = val.w;
     }
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        lo |= (uint32_t)(fv[i] >= thr) << i;
-        hi |= (uint32_t)(fv[32 + i] >= thr) << i;
-    }
+    const uint32_t lo = cmp_bits32<true>(fv, thr), hi = cmp_bits32<true>(fv + 32, thr);
     uint64_t sel = ((uint64_t)hi << 32) | lo;
     const int n_ge = __popcll(sel);
     if (n_ge == keep) return sel;
     if (n_ge > keep) {
         // ties at the threshold: everything above it, then the tied channels
-        uint32_t glo = 0, ghi = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            glo |= (uint32_t)(fv[i] > thr) << i;
-            ghi |= (uint32_t)(fv[32 + i] > thr) << i;
-        }
+        const uint32_t glo = cmp_bits32<false>(fv, thr), ghi = cmp_bits32<false>(fv + 32, thr);
         const uint64_t gt = ((uint64_t)ghi << 32) | glo;
         return gt | lowest_bits(sel & ~gt, keep - __popcll(gt));
     }
