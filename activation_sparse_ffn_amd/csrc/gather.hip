@@ -394,16 +394,6 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     }
     __syncthreads();
 
-    // kept rows of W_d^T: thread tid owns columns 8 tid .. 8 tid + 7. The
-    // gathered weight rows are read once per token and go through the
-    // caches as streaming loads (measured: ~1 us less per layer).
-    Raw<uint16_t> rd[KEEP];
-#pragma unroll
-    for (int k = 0; k < KEEP; ++k) {
-        const int j = __builtin_amdgcn_readfirstlane(sid[k]);
-        rd[k].load_stream(WdT + (size_t)j * D + 8 * tid);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of gate/up
 
     // gate / up: wave wv takes kept slots wv, wv + NW, ...
     Raw<uint16_t> rg[CPW][NCX], ru[CPW][NCX];
@@ -417,6 +407,16 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
             rg[k][m].load_stream(gr + 8 * (lane + kWave * m));
             ru[k][m].load_stream(ur + 8 * (lane + kWave * m));
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // kept rows of W_d^T, requested after gate/up's: loads complete in order,
+    // so gate/up can start while these stream in. Thread tid owns columns
+    // 8 tid .. 8 tid + 7.
+    Raw<uint16_t> rd[KEEP];
+#pragma unroll
+    for (int k = 0; k < KEEP; ++k) {
+        const int j = __builtin_amdgcn_readfirstlane(sid[k]);
+        rd[k].load_stream(WdT + (size_t)j * D + 8 * tid);
     }
     __builtin_amdgcn_sched_barrier(0);
     float u[CPW], v[CPW];
