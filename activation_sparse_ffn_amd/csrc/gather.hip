@@ -324,8 +324,10 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ partia
 // of 8 waves per (token, bank) runs predictor layer 2 on the bank's 64 rows of
 // B, the bank top-k, gate/up on the KEEP kept rows and the bank's share of the
 // down projection over all d columns, written as one partial row of y.
-// The kept rows of W_d^T are requested right after the top-k so that they
-// stream in while gate/up is computed.
+// Every wave runs the bank top-k itself (the mask is wave-uniform, so the
+// kept channels come out of it in scalar registers); the kept rows of W_g
+// and W_u are requested first and those of W_d^T right after, so gate/up
+// starts while W_d^T streams in.
 // ---------------------------------------------------------------------------
 constexpr int kFusedD = 4096;
 
@@ -341,8 +343,7 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     static_assert(KEEP % NW == 0, "kept channels split evenly over the waves");
     __shared__ uint4 xs[D / 8];
     __shared__ float sp[kBank];
-    __shared__ int sid[KEEP];
-    __shared__ float spk[KEEP], sh[KEEP];
+    __shared__ float sh[KEEP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nb = d_i / kBank;
@@ -379,27 +380,35 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     }
     __syncthreads();
 
-    // bank top-k
+    // bank top-k, run by every wave: the mask is wave-uniform, so each wave
+    // finds the kept channels in it (slot k = the k-th set bit) without an
+    // exchange through LDS
+    const float pl = sp[lane];
+    const uint64_t sel = wave_bank_topk(rank_key(pl), KEEP);
     if (wv == 0) {
-        const float p = sp[lane];
-        const uint64_t sel = wave_bank_topk(rank_key(p), KEEP);
-        const int j = (int)b * kBank + lane;
-        if (logits) logits[(size_t)t * d_i + j] = p;
+        if (logits) logits[(size_t)t * d_i + (size_t)b * kBank + lane] = pl;
         if (lane == 0) mask[(size_t)t * nb + b] = sel;
-        if ((sel >> lane) & 1ull) {
-            const int slot = (int)lanes_below(sel);
-            sid[slot] = j;
-            spk[slot] = p;
-        }
     }
-    __syncthreads();
+    auto drop = [](uint64_t m, int n) {          // m without its n lowest set bits
+        for (int i = 0; i < n; ++i) m &= m - 1;
+        return m;
+    };
 
 
     // gate / up: wave wv takes kept slots wv, wv + NW, ...
     Raw<uint16_t> rg[CPW][NCX], ru[CPW][NCX];
+    int mine[CPW];                                  // this wave's kept channels in the bank
+    {
+        uint64_t m = drop(sel, wv);
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            mine[k] = __builtin_ctzll(m);
+            m = drop(m, NW);
+        }
+    }
 #pragma unroll
     for (int k = 0; k < CPW; ++k) {
-        const int j = __builtin_amdgcn_readfirstlane(sid[wv + NW * k]);
+        const int j = (int)b * kBank + mine[k];
         const uint16_t* gr = Wg + (size_t)j * D;
         const uint16_t* ur = Wu + (size_t)j * D;
 #pragma unroll
@@ -413,10 +422,14 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     // so gate/up can start while these stream in. Thread tid owns columns
     // 8 tid .. 8 tid + 7.
     Raw<uint16_t> rd[KEEP];
+    {
+        uint64_t m = sel;
 #pragma unroll
-    for (int k = 0; k < KEEP; ++k) {
-        const int j = __builtin_amdgcn_readfirstlane(sid[k]);
-        rd[k].load_stream(WdT + (size_t)j * D + 8 * tid);
+        for (int k = 0; k < KEEP; ++k) {
+            const int j = (int)b * kBank + __builtin_ctzll(m);
+            m &= m - 1;
+            rd[k].load_stream(WdT + (size_t)j * D + 8 * tid);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     float u[CPW], v[CPW];
@@ -444,7 +457,8 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
         const float uu = wave_sum(u[k]), vv = wave_sum(v[k]);
         if (lane == 0) {
             const int slot = wv + NW * k;
-            const float sg = gate ? sigmoidf_dev(uu) : sigmoidf_dev(spk[slot]);
+            const float pk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), mine[k]));
+            const float sg = gate ? sigmoidf_dev(uu) : sigmoidf_dev(pk);
             sh[slot] = sg * uu * vv;
         }
     }
