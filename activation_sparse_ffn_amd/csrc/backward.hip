@@ -14,8 +14,8 @@
 //
 // Steps, for T tokens (bf16 operands, fp32 accumulation, fp32 gradients):
 //   z = bf16(x A^T), p = z B^T + bias          recomputed forward logits
-//   g_h = g_y W_d                               every channel (W_d^T packed)
-//   U = x W_g^T, V = x W_u^T                    dense, fp32
+//   g_h = g_y W_d                               every channel (W_d^T packed), bf16
+//   U = x W_g^T, V = x W_u^T                    dense, bf16
 //   k_bwd_tile: theta, h, g_u, g_v, g_p         one workgroup per (64 tokens, bank)
 //   g_W_d = g_y^T h, g_W_g = g_u^T x, g_W_u = g_v^T x, g_B = g_p^T z,
 //   g_z = g_p B, g_A = g_z^T x, g_bias = sum_t g_p,
@@ -49,8 +49,8 @@ __device__ __forceinline__ float wave_max(float v) {
 // weight gradients, which contract over tokens); g_p's column sums over the
 // block go to colpart[block][d_i] for g_bias.
 constexpr int kBwdTok = 64;
-__global__ __launch_bounds__(256) void k_bwd_tile(const float* __restrict__ p, const float* __restrict__ U,
-                                                  const float* __restrict__ V, const float* __restrict__ g_h,
+__global__ __launch_bounds__(256) void k_bwd_tile(const float* __restrict__ p, const uint16_t* __restrict__ U,
+                                                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ g_h,
                                                   const uint64_t* __restrict__ mask, int64_t T, int nb, int Tp,
                                                   int gate, int keep, float inv_tau,
                                                   uint16_t* __restrict__ g_u, uint16_t* __restrict__ g_v,
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_bwd_tile(const float* __restrict__ p, c
         if (t < T) {
             const int64_t w = t * nb + b;
             const int64_t o = t * (int64_t)d_i + j;
-            const float pv = p[o], u = U[o], v = V[o], gh = g_h[o];
+            const float pv = p[o], u = bf16_to_f32(U[o]), v = bf16_to_f32(V[o]), gh = bf16_to_f32(g_h[o]);
             const bool kept = (mask[w] >> lane) & 1ull;
             const float m = kept ? 1.f : 0.f;
             // threshold: midpoint of the smallest kept and the largest dropped logit
@@ -152,7 +152,7 @@ constexpr size_t kWsAlign = 256;
 size_t up(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 struct BwdLayout {
-    size_t z16, p32, gh32, U32, V32, gu16, gv16, gp16, gz16, colpart;
+    size_t z16, p32, gh16, U16, V16, gu16, gv16, gp16, gz16, colpart;
     size_t GT, hT, XT, guT, gvT, gpT, zT, gzT, BT, AT, WgT, WuT, total;
 };
 
@@ -164,17 +164,17 @@ BwdLayout layout(int64_t T, int d, int d_i, int r, bool weights_t) {
     auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
     L.z16 = take((size_t)T * r * 2);
     L.p32 = take(tdi * 4);
-    L.gh32 = take(tdi * 4);
-    // U32 is dead outside [UV GEMM, k_bwd_tile]: the other GEMMs use it for
-    // their K-split partials
+    L.gh16 = take(tdi * 2);
+    // U16 is dead outside [UV GEMM, k_bwd_tile]: the other GEMMs use its
+    // space for their fp32 K-split partials
     const int64_t Tq = (int64_t)Tp;
     const size_t part = std::max({gemm_nt_partial_floats(T, r, d), gemm_nt_partial_floats(T, d_i, r),
                                   gemm_nt_partial_floats(T, d_i, d), gemm_nt_partial_floats(d, d_i, (int)Tq),
                                   gemm_nt_partial_floats(d_i, d, (int)Tq), gemm_nt_partial_floats(d_i, r, (int)Tq),
                                   gemm_nt_partial_floats(T, r, d_i), gemm_nt_partial_floats(r, d, (int)Tq),
                                   gemm_nt_partial_floats(T, d, r), gemm_nt_partial_floats(T, d, d_i)});
-    L.U32 = take(std::max(tdi, part) * 4);
-    L.V32 = take(tdi * 4);
+    L.U16 = take(std::max(tdi * 2, part * 4));
+    L.V16 = take(tdi * 2);
     L.gu16 = take(tdi * 2);
     L.gv16 = take(tdi * 2);
     L.colpart = take(Tp / 64 * (size_t)d_i * 4);
@@ -218,9 +218,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     void* ws = a.ws;
     uint16_t* z16 = at<uint16_t>(ws, L.z16);
     float* p32 = at<float>(ws, L.p32);
-    float* gh32 = at<float>(ws, L.gh32);
-    float* U32 = at<float>(ws, L.U32);
-    float* V32 = at<float>(ws, L.V32);
+    uint16_t* gh16 = at<uint16_t>(ws, L.gh16);
+    uint16_t* U16 = at<uint16_t>(ws, L.U16);
+    uint16_t* V16 = at<uint16_t>(ws, L.V16);
+    float* split = at<float>(ws, L.U16);           // K-split partials of the other GEMMs
     uint16_t* gu16 = at<uint16_t>(ws, L.gu16);
     uint16_t* gv16 = at<uint16_t>(ws, L.gv16);
     float* colpart = at<float>(ws, L.colpart);
@@ -242,12 +243,12 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; return e == hipSuccess; };
 
     // recomputed forward: z, p, dense U and V; g_h for every channel
-    ok(launch_gemm_nt(a.x, a.A, T, r, d, z16, GemmOut::BF16, s, nullptr, U32));
-    ok(launch_gemm_nt(z16, a.B, T, d_i, r, p32, GemmOut::F32, s, a.bias, U32));
-    ok(launch_gemm_nt(a.g_y, a.W_dT, T, d_i, d, gh32, GemmOut::F32, s, nullptr, U32));
-    ok(launch_uv_gemm(a.x, a.W_g, a.W_u, T, d_i, d, U32, V32, s));
-    hipLaunchKernelGGL(k_bwd_tile, dim3((unsigned)(Tp / kBwdTok), (unsigned)nb), dim3(256), 0, s, p32, U32, V32,
-                       gh32, a.mask, T, nb, Tp, a.gate, a.keep, a.inv_tau, gu16, gv16, gp16, hT, guT, gvT, gpT,
+    ok(launch_gemm_nt(a.x, a.A, T, r, d, z16, GemmOut::BF16, s, nullptr, split));
+    ok(launch_gemm_nt(z16, a.B, T, d_i, r, p32, GemmOut::F32, s, a.bias, split));
+    ok(launch_gemm_nt(a.g_y, a.W_dT, T, d_i, d, gh16, GemmOut::BF16, s, nullptr, split));
+    ok(launch_uv_gemm(a.x, a.W_g, a.W_u, T, d_i, d, U16, V16, s));
+    hipLaunchKernelGGL(k_bwd_tile, dim3((unsigned)(Tp / kBwdTok), (unsigned)nb), dim3(256), 0, s, p32, U16, V16,
+                       gh16, a.mask, T, nb, Tp, a.gate, a.keep, a.inv_tau, gu16, gv16, gp16, hT, guT, gvT, gpT,
                        colpart);
     ok(hipGetLastError());
     if (a.g_bias) {
@@ -259,24 +260,24 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     ok(launch_transpose(Dt::BF16, a.g_y, GT, (int)T, d, s, Tp));
     ok(launch_transpose(Dt::BF16, a.x, XT, (int)T, d, s, Tp));
     ok(launch_transpose(Dt::BF16, z16, zT, (int)T, r, s, Tp));
-    ok(launch_gemm_nt(GT, hT, d, d_i, Tp, a.g_Wd, GemmOut::F32, s, nullptr, U32));
-    ok(launch_gemm_nt(guT, XT, d_i, d, Tp, a.g_Wg, GemmOut::F32, s, nullptr, U32));
-    ok(launch_gemm_nt(gvT, XT, d_i, d, Tp, a.g_Wu, GemmOut::F32, s, nullptr, U32));
-    ok(launch_gemm_nt(gpT, zT, d_i, r, Tp, a.g_B, GemmOut::F32, s, nullptr, U32));
+    ok(launch_gemm_nt(GT, hT, d, d_i, Tp, a.g_Wd, GemmOut::F32, s, nullptr, split));
+    ok(launch_gemm_nt(guT, XT, d_i, d, Tp, a.g_Wg, GemmOut::F32, s, nullptr, split));
+    ok(launch_gemm_nt(gvT, XT, d_i, d, Tp, a.g_Wu, GemmOut::F32, s, nullptr, split));
+    ok(launch_gemm_nt(gpT, zT, d_i, r, Tp, a.g_B, GemmOut::F32, s, nullptr, split));
     // the predictor's input side
     ok(launch_transpose(Dt::BF16, a.B, BT, d_i, r, s));
-    ok(launch_gemm_nt(gp16, BT, T, r, d_i, gz16, GemmOut::BF16, s, nullptr, U32));
+    ok(launch_gemm_nt(gp16, BT, T, r, d_i, gz16, GemmOut::BF16, s, nullptr, split));
     ok(launch_transpose(Dt::BF16, gz16, gzT, (int)T, r, s, Tp));
-    ok(launch_gemm_nt(gzT, XT, r, d, Tp, a.g_A, GemmOut::F32, s, nullptr, U32));
+    ok(launch_gemm_nt(gzT, XT, r, d, Tp, a.g_A, GemmOut::F32, s, nullptr, split));
     // g_x = g_z A + g_u W_g + g_v W_u
     ok(launch_transpose(Dt::BF16, a.A, AT, r, d, s));
     if (!have_wt) {
         ok(launch_transpose(Dt::BF16, a.W_g, at<uint16_t>(ws, L.WgT), d_i, d, s));
         ok(launch_transpose(Dt::BF16, a.W_u, at<uint16_t>(ws, L.WuT), d_i, d, s));
     }
-    ok(launch_gemm_nt(gz16, AT, T, d, r, a.g_x, GemmOut::F32, s, nullptr, U32));
-    ok(launch_gemm_nt(gu16, WgT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, U32));
-    ok(launch_gemm_nt(gv16, WuT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, U32));
+    ok(launch_gemm_nt(gz16, AT, T, d, r, a.g_x, GemmOut::F32, s, nullptr, split));
+    ok(launch_gemm_nt(gu16, WgT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, split));
+    ok(launch_gemm_nt(gv16, WuT, T, d, d_i, a.g_x, GemmOut::F32_ACC, s, nullptr, split));
     return e;
 }
 

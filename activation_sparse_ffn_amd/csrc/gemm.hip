@@ -44,7 +44,7 @@ struct GemmParams {
     uint16_t* gate_w;    // fp16 gate tiles
     int keep;
     int dense;           // EPI_GATEUP without gate tiles: every channel kept (silu gate)
-    float* Cf2;          // EPI_UV: fp32 [M, N] receives V (Cf receives U)
+    uint16_t* Cb2;       // EPI_UV: bf16 [M, N] receives V (Cb receives U)
 };
 
 constexpr int BM = 128, BN = 128, BK = 32;
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
                 } else if constexpr (EPI == EPI_F32_ACC) {
                     p.Cf[o] += acc[0][i][j][v];
                 } else if constexpr (EPI == EPI_UV) {
-                    p.Cf[o] = acc[0][i][j][v];
-                    p.Cf2[o] = acc[NB - 1][i][j][v];
+                    p.Cb[o] = f32_to_bf16(acc[0][i][j][v]);
+                    p.Cb2[o] = f32_to_bf16(acc[NB - 1][i][j][v]);
                 } else {
                     const float u = acc[0][i][j][v];
                     const float vv = acc[NB - 1][i][j][v];
@@ -669,8 +669,8 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
                 } else if constexpr (EPI == EPI_F32_ACC) {
                     p.Cf[o] += acc[i][j][v];
                 } else if constexpr (EPI == EPI_UV) {
-                    p.Cf[o] = acc[i][j][v];
-                    p.Cf2[o] = acc[i][j + NJ / 2][v];
+                    p.Cb[o] = f32_to_bf16(acc[i][j][v]);
+                    p.Cb2[o] = f32_to_bf16(acc[i][j + NJ / 2][v]);
                 } else {
                     const float u = acc[i][j][v];
                     const float vv = acc[i][j + NJ / 2][v];
@@ -875,9 +875,9 @@ hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int64_t M, int N
 }
 
 hipError_t launch_uv_gemm(const uint16_t* x, const uint16_t* W_g, const uint16_t* W_u, int64_t T, int d_i,
-                          int d, float* U, float* V, hipStream_t s) {
+                          int d, uint16_t* U, uint16_t* V, hipStream_t s) {
     GemmParams g{};
-    g.A = x; g.B0 = W_g; g.B1 = W_u; g.M = T; g.N = d_i; g.K = d; g.Cf = U; g.Cf2 = V;
+    g.A = x; g.B0 = W_g; g.B1 = W_u; g.M = T; g.N = d_i; g.K = d; g.Cb = U; g.Cb2 = V;
     if (T >= 256 && d % TK == 0) gemm256<EPI_UV>(g, s, nullptr, 0);
     else gemm<EPI_UV>(g, s, nullptr, 0);
     return hipGetLastError();

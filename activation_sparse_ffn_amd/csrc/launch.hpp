@@ -150,9 +150,9 @@ enum class GemmOut { F32, F32_ACC, BF16 };   // store fp32, add to fp32, store b
 size_t gemm_nt_partial_floats(int64_t M, int N, int K);
 hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int64_t M, int N, int K, void* C,
                           GemmOut out, hipStream_t s, const float* bias = nullptr, float* partial = nullptr);
-// dense U = X W_g^T and V = X W_u^T, fp32 [T, d_i] each
+// dense U = X W_g^T and V = X W_u^T, rounded to bf16 [T, d_i] each
 hipError_t launch_uv_gemm(const uint16_t* x, const uint16_t* W_g, const uint16_t* W_u, int64_t T, int d_i,
-                          int d, float* U, float* V, hipStream_t s);
+                          int d, uint16_t* U, uint16_t* V, hipStream_t s);
 
 // ---- backward pass (bf16 layers, predictor or silu gate) ----------------------
 struct BwdArgs {
