@@ -23,6 +23,8 @@ pytestmark = [pytest.mark.gpu,
 
 REL_L2 = 2e-2
 GAP = 1e-3
+SNAN = np.array([0x7F800001], dtype=np.uint32).view(np.float32)[0]      # signaling NaN bits
+NEG_NAN = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]   # quiet NaN, sign set
 
 
 def dev(a):
@@ -134,6 +136,8 @@ def _specials(T=6, d_i=256):
     p[4, 5:60] = np.nan
     p[5, 128:192] = np.arange(64, dtype=np.float32)[::-1]
     p[5, 192:256] = np.float32(1e-45) * (np.arange(64) % 3 - 1)   # subnormals and zeros
+    p[3, 0:64:5] = SNAN                                              # signaling and negative NaNs
+    p[3, 1:64:7] = NEG_NAN
     return p
 
 
@@ -169,6 +173,9 @@ def test_bank_topk_many_banks_per_wave(keep):
     p[8, 1::2] = -np.inf
     p[9, :64] = np.where(np.arange(64) % 2, -0.0, 0.0)
     p[10, 128:192] = np.float32(1e-45) * (np.arange(64) % 3 - 1)
+    p[11, 0:64:3] = SNAN
+    p[11, 1:64:5] = NEG_NAN
+    p[12, 64:128] = SNAN                      # a bank of signaling NaNs only
     mask, ids = sffn.bank_topk(dev(p), keep=keep, return_ids=True)
     torch.cuda.synchronize()
     m = o.bank_topk_mask(p, 64, keep)
@@ -188,6 +195,7 @@ def test_bank_topk_persistent_chunks(T, keep):
     p[::5] = np.random.default_rng(21).standard_normal((len(p[::5]), 1024)).astype(np.float32)
     p[T - 1, 960:] = np.nan                   # the very last bank: NaNs only
     p[T - 2, 0:64:2] = -np.inf
+    p[T - 3, 0:64:4] = SNAN
     mask, ids = sffn.bank_topk(dev(p), keep=keep, return_ids=True)
     torch.cuda.synchronize()
     m = o.bank_topk_mask(p, 64, keep)
