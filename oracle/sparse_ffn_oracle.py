@@ -156,7 +156,8 @@ def _beats(v: np.ndarray) -> np.ndarray:
     """beats[..., a, b] is True when channel a precedes channel b in the
     ranking order of one bank: larger value first, -0 == +0, NaN after every
     number, equal values by lower index."""
-    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(invalid="ignore"):        # signaling NaNs widen to NaN
+        v = np.asarray(v, dtype=np.float64)
     nan = np.isnan(v)
     v = np.where(v == 0.0, 0.0, v)
     n = v.shape[-1]
