@@ -527,9 +527,9 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         mma(xa, xb); frags(cur, 3, ya, yb); interleave();
         landed();                                   // slab kt + 1 is in LDS, `cur` is free
         if (kt + 2 < kt_n) fetch((kt + 2) * TK, cur);
-        else if (gtile != nullptr && kt + 1 == kt_n) fetch_gate(gtile, cur);
+        else if (gtile != nullptr && (kt + 2 == kt_n || kt_n == 1)) fetch_gate(gtile, cur);
         mma(ya, yb);
-        frags(nxt, 0, xa, xb);       // after the last step: stale, unused (no load writes nxt then)
+        frags(nxt, 0, xa, xb);       // after the last step: stale, unused
         interleave();
     };
 
@@ -551,7 +551,9 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         step(buf1, buf0, kt + 1);
     }
     if (kt < kt_n) step(buf0, buf1, kt);       // odd count: the last slab is in buf0
-    char* gbuf = (kt_n & 1) ? buf0 : buf1;     // the last step's `cur`
+    // the gate tile went into the second-to-last step's `cur`, which is the
+    // last step's `nxt` (one step only: that step's `cur`, buf0)
+    char* gbuf = kt_n == 1 ? buf0 : ((kt_n & 1) ? buf1 : buf0);
 
     // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2)
     // + 4 (lane >> 5); for gate/up, tile j < NJ / 2 holds u and tile
