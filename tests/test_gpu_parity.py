@@ -274,6 +274,34 @@ def test_forward_batched_full(full_layer, ffn_full_bias):
     assert 0.5 < frac < 1.0      # partial overlap across tokens
 
 
+def test_concurrent_forwards_on_two_streams(ffn_full_bias):
+    """Forwards of one layer on two streams at once, each with its own
+    workspace (the interface allows it), give the bits of the same forwards
+    run one after another: decode, the skinny path and the MFMA path."""
+    Ts = [1, 32, 300, 1, 32, 300]
+    xs = [dev(wl.make_tokens(wl.FULL, T, seed=900 + i)) for i, T in enumerate(Ts)]
+    ref = []
+    for x in xs:
+        ref.append(ffn_full_bias(x, return_mask=True))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.empty(ffn_full_bias.workspace_size(300), dtype=torch.uint8, device="cuda") for _ in streams]
+    outs = [None] * len(xs)
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for i, x in enumerate(xs):
+        k = i % 2
+        with torch.cuda.stream(streams[k]):
+            y = torch.empty_like(x)
+            mask = torch.empty((x.shape[0], 224), dtype=torch.int64, device="cuda")
+            ffn_full_bias(x, y=y, mask=mask, workspace=wss[k])
+            outs[i] = (y, mask)
+    torch.cuda.synchronize()
+    for (y, m), (yr, mr) in zip(outs, ref):
+        assert torch.equal(m, mr)
+        assert torch.equal(y.view(torch.int16), yr.view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [5, 40, 64, 130, 300])
 def test_forward_mfma_ragged_full(full_layer, ffn_full, T):
     x = wl.make_tokens(wl.FULL, T, seed=300 + T)
