@@ -175,9 +175,10 @@ sffn_status_t sparse_ffn_set_stage_events(sffn_handle_t h, void* const* events,
 const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i);
 
 /* Workspace bytes sparse_ffn_backward needs for T tokens (0 for T <= 0 or
- * a null handle). About 10 fp32/bf16 [T, d_i] buffers plus the transposed
- * weights (W_g^T and W_u^T only without SFFN_FLAG_BACKWARD): ~2.4 GB at
- * T = 4096, d = 4096, d_i = 14336. */
+ * a null handle). One fp32 and about ten bf16 [T, d_i] buffers, the
+ * token-transposed operands and the transposed predictor weights, plus
+ * W_g^T and W_u^T without SFFN_FLAG_BACKWARD: ~1.5 GB at T = 4096, d = 4096,
+ * d_i = 14336 with the flag, ~1.75 GB without. */
 size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T);
 
 /* Backward pass of a forward of T tokens ("Continual LLM Upcycling",
