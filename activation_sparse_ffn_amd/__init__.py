@@ -123,6 +123,22 @@ def _need_gpu(*ts: torch.Tensor):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+def _need_buffer(t: torch.Tensor, name: str, shape, dtype, device: torch.device):
+    """A caller-supplied output or scratch tensor: shape, dtype, device and
+    contiguity are checked before its address reaches the library, which
+    writes through it without knowing its extent."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the layer on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def bank_topk(logits: torch.Tensor, keep: int = 16, return_ids: bool = False,
               mask_out: Optional[torch.Tensor] = None, ids_out: Optional[torch.Tensor] = None):
     """Bank-wise hard top-k over fp32 logits [T, d_i] (banks of 64).
@@ -139,8 +155,12 @@ def bank_topk(logits: torch.Tensor, keep: int = 16, return_ids: bool = False,
     nb = d_i // 64
     if mask_out is None:
         mask_out = torch.empty((T, nb), dtype=torch.int64, device=logits.device)
+    else:
+        _need_buffer(mask_out, "mask_out", (T, nb), torch.int64, logits.device)
     if return_ids and ids_out is None:
         ids_out = torch.empty((T, nb * keep), dtype=torch.int16, device=logits.device)
+    elif return_ids:
+        _need_buffer(ids_out, "ids_out", (T, nb * keep), torch.int16, logits.device)
     _check(lib, lib.bank_topk(_ptr(logits), T, d_i, keep, _ptr(mask_out),
                               _ptr(ids_out) if return_ids else None, _stream(logits.device)))
     return (mask_out, ids_out) if return_ids else mask_out
@@ -194,7 +214,7 @@ class SparseFFN:
             ctypes.byref(self.cfg), _ptr(W_g), _ptr(W_u), _ptr(W_d), _ptr(A), _ptr(B), _ptr(bias),
             _ptr(self.packed), size, _stream(self.device), ctypes.byref(h)))
         self._h = h
-        self._ws = None
+        self._ws = {}
         self.has_bias = bias is not None
 
     @property
@@ -209,11 +229,18 @@ class SparseFFN:
         return int(self._lib.sparse_ffn_workspace_size(self._h, T))
 
     def workspace(self, T: int) -> torch.Tensor:
-        """A workspace tensor for T tokens (cached, grown on demand)."""
+        """A workspace tensor for T tokens on the current stream (cached per
+        stream, grown on demand). Forwards on different streams never share
+        one, and a grown workspace replaces the old one only on its own
+        stream, where torch's allocator reuses the freed block after the work
+        already queued there."""
         need = self.workspace_size(T)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
-        return self._ws
+        key = torch.cuda.current_stream(self.device).cuda_stream
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
 
     def forward(self, x: torch.Tensor, return_mask: bool = False, return_logits: bool = False,
                 y: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
@@ -222,12 +249,24 @@ class SparseFFN:
         if x.dtype != self.dtype or x.dim() != 2 or x.shape[1] != self.d:
             raise ValueError(f"x must be [T, {self.d}] {self.dtype}")
         T = x.shape[0]
+        if x.device != self.device:
+            raise ValueError(f"x is on {x.device}, the layer on {self.device}")
         if y is None:
             y = torch.empty_like(x)
+        else:
+            _need_buffer(y, "y", (T, self.d), self.dtype, self.device)
         if return_mask and mask is None:
             mask = torch.empty((T, self.d_i // 64), dtype=torch.int64, device=self.device)
+        elif mask is not None:
+            _need_buffer(mask, "mask", (T, self.d_i // 64), torch.int64, self.device)
         if return_logits and logits is None:
             logits = torch.empty((T, self.d_i), dtype=torch.float32, device=self.device)
+        elif logits is not None:
+            _need_buffer(logits, "logits", (T, self.d_i), torch.float32, self.device)
+        if workspace is not None:
+            _need_buffer(workspace, "workspace", None, torch.uint8, self.device)
+            if workspace.dim() != 1:
+                raise ValueError("workspace must be a 1-D uint8 tensor")
         ws = workspace if workspace is not None else self.workspace(T)
         _check(self._lib, self._lib.sparse_ffn_forward(
             self._h, _ptr(x), T, _ptr(y), _ptr(mask) if return_mask or mask is not None else None,
@@ -263,6 +302,8 @@ class SparseFFN:
                "W_u": torch.empty((self.d_i, self.d), **f32), "W_d": torch.empty((self.d, self.d_i), **f32),
                "bias": torch.empty(self.d_i, **f32) if self.has_bias else None}
         need = int(self._lib.sparse_ffn_backward_workspace_size(self._h, T))
+        if workspace is not None:
+            _need_buffer(workspace, "workspace", None, torch.uint8, self.device)
         ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8,
                                                                    device=self.device)
         _check(self._lib, self._lib.sparse_ffn_backward(

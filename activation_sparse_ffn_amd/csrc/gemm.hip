@@ -736,15 +736,19 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     if (!a.need_pred) {
         // every channel kept with the silu gate and no logits asked for: no
         // predictor and no top-k. The 256-wide gate/up epilogue keeps every
-        // channel by itself; the mask is written when asked for or read.
+        // channel by itself when whole 128-column gate tiles cover d_i (its
+        // in-place path stores all 128 columns of a tile); otherwise the
+        // general epilogue reads the all-ones mask and skips columns >= d_i.
+        // The mask is written when asked for or read.
         skip_range(a.events, 0, 3, s);
-        if (a.mask_requested || !big) {
+        const bool dense_tiles = big && a.d_i % kGateTileCols == 0;
+        if (a.mask_requested || !dense_tiles) {
             const hipError_t e = launch_fill_mask(a.mask, a.T * (a.d_i / kBank), s);
             if (e != hipSuccess) return e;
         }
         g = GemmParams{};
         g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;
-        g.mask = a.mask; g.gate = a.gate; g.dense = big ? 1 : 0;
+        g.mask = a.mask; g.gate = a.gate; g.dense = dense_tiles ? 1 : 0;
         if (big) gemm256<EPI_GATEUP>(g, s, a.events, 3);
         else gemm<EPI_GATEUP>(g, s, a.events, 3);
         g = GemmParams{};

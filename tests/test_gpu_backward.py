@@ -103,3 +103,27 @@ def test_backward_with_packed_weight_transposes(mid_layer, T):
     lib = sffn.load_library()
     assert lib.sparse_ffn_backward_workspace_size(ready._h, T) \
         == lib.sparse_ffn_backward_workspace_size(plain._h, T) - 4 * MID.d * MID.d_i
+
+
+# d = 4096, d_i = 1024, rank 64 at T = 2880: the g_x GEMMs (M = T, N = d)
+# have 12 x 16 = 192 output tiles of 256 x 256, enough to run on the 256-wide
+# kernel; g_z A (K = rank = 64) stores fp32 in a single K step, and g_u W_g,
+# g_v W_u then add into g_x in the accumulating epilogue.
+WIDE_GX = wl.LayerShape(d=4096, d_i=1024, rank=64)
+
+
+@pytest.fixture(scope="module")
+def wide_gx_layer():
+    return wl.make_layer(WIDE_GX, seed=31, bias_var=0.5)
+
+
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_backward_256_wide_gx_gemms(wide_gx_layer, gate):
+    run_and_check(wide_gx_layer, 2880, gate, 16, 1.0, seed=2880)
+
+
+def test_backward_full_layer_biased_256_wide_logits(full_layer):
+    """T = 1024 on the full layer with a bias: the recomputed logits
+    p = z B^T + b have 4 x 56 = 224 tiles of 256 x 256 and take the biased
+    256-wide fp32 GEMM, the one a 4096-token chunk runs."""
+    run_and_check(full_layer, 1024, "pred", 16, 1.0, seed=1024)

@@ -204,12 +204,47 @@ def test_bank_topk_persistent_chunks(T, keep):
     np.testing.assert_array_equal(ids_np, np.nonzero(m)[1].reshape(len(p), -1))
 
 
-def test_bank_topk_stress_full_size():
-    """32768 x 14336 fp32 logits with 5% exact ties per bank: the oracle on a
-    seeded sample of tokens, structural properties on every bank."""
+def assert_topk_valid_on_gpu(mask, logits, keep=16, rows_per_pass=4096):
+    """Every row of a GPU mask is THE bank top-k of its NaN-free fp32 logits,
+    checked on the GPU: exactly `keep` bits per word; the smallest kept logit
+    of a bank is >= its largest dropped one (IEEE compare: -0 == +0); and
+    where they are equal, every kept channel holding that value has a lower
+    index than every dropped one. These conditions single out the unique
+    mask of the ranking (value, then lower index). Returns the number of
+    banks whose keep boundary falls inside a tie."""
+    T, nb = mask.shape
+    assert logits.shape == (T, nb * 64)
+    assert not bool(torch.isnan(logits).any()), "the check covers NaN-free logits"
+    ties = 0
+    lanes = torch.arange(64, device=mask.device)
+    for r0 in range(0, T, rows_per_pass):
+        m = mask[r0:r0 + rows_per_pass]
+        v = logits[r0:r0 + rows_per_pass].view(-1, nb, 64)
+        bits = ((m.unsqueeze(-1) >> lanes) & 1).bool()
+        assert bool((bits.sum(-1) == keep).all()), "popcount"
+        kmin = torch.where(bits, v, torch.full_like(v, float("inf"))).amin(-1)
+        dmax = torch.where(bits, torch.full_like(v, float("-inf")), v).amax(-1)
+        assert bool((kmin >= dmax).all()), "a dropped logit above a kept one"
+        tie = dmax == kmin
+        idx = lanes.expand_as(v)
+        at_kmin = v == kmin.unsqueeze(-1)
+        last_kept = torch.where(bits & at_kmin, idx, torch.full_like(idx, -1)).amax(-1)
+        first_dropped = torch.where(~bits & at_kmin, idx, torch.full_like(idx, 99)).amin(-1)
+        assert bool((last_kept[tie] < first_dropped[tie]).all()), "tie not broken to the lower index"
+        ties += int(tie.sum())
+    return ties
+
+
+@pytest.mark.parametrize("ties", ["random", "boundary"])
+def test_bank_topk_stress_full_size(ties):
+    """32768 x 14336 fp32 logits with 5% exact ties per bank (copies of
+    random in-bank values, or 3 copies of each bank's 16th-largest value on
+    positions below it, so that every bank's boundary falls inside a tie):
+    the oracle on a seeded sample of tokens, and the complete validity check
+    of the unique mask on every bank, on the GPU."""
     import activation_sparse_ffn_amd as sffn
-    cfg = wl.CONFIGS["topk_stress"]
-    p = wl.make_stress_logits(T=cfg["T"], d_i=cfg["d_i"], seed=0, tie_frac=cfg["tie_frac"])
+    cfg = wl.CONFIGS["topk_stress" if ties == "random" else "topk_stress_boundary"]
+    p = wl.make_stress_logits(T=cfg["T"], d_i=cfg["d_i"], seed=0, tie_frac=cfg["tie_frac"], ties=ties)
     pd = dev(p)
     mask, ids = sffn.bank_topk(pd, keep=16, return_ids=True)
     torch.cuda.synchronize()
@@ -219,21 +254,10 @@ def test_bank_topk_stress_full_size():
     sample = np.sort(np.random.default_rng(0).choice(32768, size=96, replace=False))
     sample = np.concatenate([[0], sample, [32767]])
     np.testing.assert_array_equal(w[sample], o.mask_to_words(o.bank_topk_mask(p[sample], 64, 16)))
-    # every kept logit >= every dropped logit of its bank, on the GPU
-    bits = (mask.unsqueeze(-1) >> torch.arange(64, device="cuda")) & 1
-    v = pd.view(32768, 224, 64)
-    kmin = torch.where(bits.bool(), v, torch.full_like(v, float("inf"))).amin(-1)
-    dmax = torch.where(bits.bool(), torch.full_like(v, float("-inf")), v).amax(-1)
-    assert bool((kmin >= dmax).all())
-    # on ties at the boundary the lower channel wins: a dropped value equal to
-    # the smallest kept value must sit above every kept channel holding it
-    tie = (dmax == kmin)
-    assert int(tie.sum()) > 0
-    idx = torch.arange(64, device="cuda").expand_as(v)
-    at_kmin = v == kmin.unsqueeze(-1)
-    last_kept = torch.where(bits.bool() & at_kmin, idx, torch.full_like(idx, -1)).amax(-1)
-    first_dropped = torch.where(~bits.bool() & at_kmin, idx, torch.full_like(idx, 99)).amin(-1)
-    assert bool((last_kept[tie] < first_dropped[tie]).all())
+    n_ties = assert_topk_valid_on_gpu(mask, pd, 16)
+    assert n_ties > 0
+    if ties == "boundary":
+        assert n_ties == 32768 * 224           # every bank breaks a tie at its boundary
     ids_np = ids.cpu().numpy().view(np.uint16)
     for t in sample[:8]:
         np.testing.assert_array_equal(ids_np[t], np.flatnonzero(o.words_to_mask(w[t:t + 1])[0]))
@@ -319,7 +343,8 @@ def test_forward_prefill_chunk(full_layer, ffn_full):
     rows = np.concatenate([[0, 127, 128, 4095],
                            np.random.default_rng(1).choice(4096, size=8, replace=False)])
     check_forward(full_layer, x, y, mask, logits, tokens=rows, bias=False)
-    assert (np.bitwise_count(words(mask)) == 16).all()
+    # every row's mask is the bank top-k of the logits that were ranked
+    assert_topk_valid_on_gpu(mask, logits, 16)
 
 
 def test_forward_long_context_chunks(full_layer, ffn_full):
@@ -338,6 +363,8 @@ def test_forward_long_context_chunks(full_layer, ffn_full):
     rng = np.random.default_rng(2)
     rows = np.sort(np.concatenate([c * C + rng.choice(C, size=2, replace=False) for c in range(T // C)]))
     check_forward(full_layer, x, y, mask, lg, tokens=rows, bias=False)
+    # every one of the 32768 rows' masks is the bank top-k of its logits
+    assert_topk_valid_on_gpu(mask, lg, 16)
     # the same tokens in one 4096-row call at another offset give identical rows
     y2 = ffn_full(xd[C // 2:C // 2 + C])
     torch.cuda.synchronize()
@@ -552,3 +579,54 @@ def test_mask_and_output_do_not_depend_on_logits_request(full_layer, ffn_full_bi
     gl = host(p1)
     np.testing.assert_array_equal(o.mask_to_words(o.bank_topk_mask(gl, 64, 16)), words(m1))
     assert ffn_full_bias.stage_names(T)[1] == "pred2_topk_gemm"
+
+
+# d_i = 2112 = 16.5 x 128: the last 128-column gate/up tile of the 256-wide
+# kernel is half outside the layer, and no gate tiles exist (they need whole
+# 128-column tiles).
+HALF_TILE = wl.LayerShape(d=512, d_i=2112, rank=64)
+
+
+@pytest.fixture(scope="module")
+def half_tile_layer():
+    return wl.make_layer(HALF_TILE, seed=9, bias_var=0.5)
+
+
+@pytest.mark.parametrize("T", [300, 257])
+@pytest.mark.parametrize("ask", [False, True])
+def test_dense_fallback_half_gate_tile(half_tile_layer, T, ask):
+    """keep = 64 with the silu gate (the dense fallback: no predictor, no
+    top-k) when d_i is not a multiple of 128: the 256-wide gate/up epilogue
+    must not write past the layer's last channel into the next token's row
+    or past the intermediate. Every row against the oracle, with and
+    without the mask and logits asked for."""
+    L = half_tile_layer
+    ffn = make_ffn(L, bias=True, keep=64, gate="silu")
+    x = wl.make_tokens(HALF_TILE, T, seed=T)
+    xd = dev(x)
+    if ask:
+        y, mask, logits = ffn(xd, return_mask=True, return_logits=True)
+    else:
+        y = ffn(xd)
+    torch.cuda.synchronize()
+    r = o.forward(x, L.A, L.B, L.W_g, L.W_u, L.W_d, bias=L.bias, keep=64, gate="silu")
+    yg = o.widen(host(y))
+    for t in range(T):
+        assert rel_l2(yg[t], r["y"][t]) <= REL_L2, f"token {t}"
+    if ask:
+        assert (words(mask) == np.uint64(0xFFFFFFFFFFFFFFFF)).all()
+        check_forward(L, x, y, mask, logits, bias=True, keep=64, gate="silu")
+
+
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_sparse_half_gate_tile(half_tile_layer, gate):
+    """keep = 16 at T = 300 with d_i % 128 == 64: predictor layer 2 as a
+    separate fp32 GEMM, the stand-alone bank top-k and the general gate/up
+    epilogue (mask and logits read per element), every row checked."""
+    L = half_tile_layer
+    ffn = make_ffn(L, bias=True, keep=16, gate=gate)
+    x = wl.make_tokens(HALF_TILE, 300, seed=77)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    assert ffn.stage_names(300)[2] == "bank_topk"
+    check_forward(L, x, y, mask, logits, bias=True, keep=16, gate=gate)

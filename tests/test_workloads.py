@@ -55,3 +55,30 @@ def test_tie_logits():
     p = wl.make_tie_logits(T=16, d_i=1024, seed=0)
     assert set(np.unique(p)) <= set(range(-4, 5))
     assert np.signbit(p[p == 0]).any()
+
+
+def test_boundary_ties_straddle_the_keep_boundary():
+    """The boundary variant of the stress logits: in every bank keep - 1
+    values lie above the keep-th largest and 1 + 3 equal it, so the top-k must
+    break a tie across the boundary (3 of the 4 tied channels dropped)."""
+    for keep in (16, 5):
+        p = wl.make_stress_logits(T=96, d_i=2048, seed=4, ties="boundary", keep=keep)
+        v = p.reshape(96, 32, 64)
+        kth = np.sort(v, axis=-1)[..., 64 - keep]
+        assert ((v > kth[..., None]).sum(-1) == keep - 1).all()
+        assert ((v == kth[..., None]).sum(-1) == 4).all()
+        np.testing.assert_array_equal(p, wl.make_stress_logits(T=96, d_i=2048, seed=4, ties="boundary",
+                                                               keep=keep))
+    # the oracle keeps the lowest-index tied channel only
+    p = wl.make_stress_logits(T=8, d_i=1024, seed=1, ties="boundary")
+    m = o.bank_topk_mask(p, 64, 16)
+    v = p.reshape(8, 16, 64)
+    kth = np.sort(v, axis=-1)[..., 48]
+    tied = v == kth[..., None]
+    kept_tied = m.reshape(8, 16, 64) & tied
+    assert (kept_tied.sum(-1) == 1).all()
+    first = np.argmax(tied, axis=-1)
+    assert (np.argmax(kept_tied, axis=-1) == first).all()
+    # the random-copy variant is unchanged by the new option
+    np.testing.assert_array_equal(wl.make_stress_logits(T=16, d_i=1024, seed=2),
+                                  wl.make_stress_logits(T=16, d_i=1024, seed=2, ties="random"))

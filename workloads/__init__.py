@@ -142,16 +142,44 @@ def outlier_columns(shape: LayerShape, seed: int = 0, outlier_frac: float = 0.01
 
 
 def make_stress_logits(T: int, d_i: int, seed: int = 0, bank: int = 64,
-                       tie_frac: float = 0.05) -> np.ndarray:
+                       tie_frac: float = 0.05, ties: str = "random", keep: int = 16) -> np.ndarray:
     """fp32 logits [T, d_i] ~ N(0, 1) with exact ties injected per bank.
 
-    In every bank, round(tie_frac * bank) positions are overwritten, each with
-    the value of a randomly chosen position of the same bank that is not
-    overwritten, so every bank holds at least one exact tie.
+    ties="random": in every bank, round(tie_frac * bank) positions are
+    overwritten, each with the value of a randomly chosen position of the
+    same bank that is not overwritten, so every bank holds at least one exact
+    tie.
+
+    ties="boundary": in every bank, round(tie_frac * bank) positions drawn
+    from those below the bank's keep-th largest value are overwritten with
+    that value, so every bank holds an exact tie that straddles the keep
+    boundary (keep - 1 values above it, 1 + round(tie_frac * bank) equal to
+    it).
     """
+    if ties not in ("random", "boundary"):
+        raise ValueError("ties must be 'random' or 'boundary'")
     r = _rngs(seed)
     p = r["x"].standard_normal(size=(T, d_i), dtype=np.float32)
     n_tie = int(round(tie_frac * bank))
+    if n_tie and ties == "boundary":
+        nb = d_i // bank
+        g = r["spare"]
+        below = bank - keep                # positions under the keep-th largest value
+        step = max(1, (1 << 22) // d_i)    # tokens per slice: bounded index arrays
+        for t0 in range(0, T, step):
+            pv = p[t0:t0 + step].reshape(-1, nb, bank)
+            order = np.argpartition(pv, below, axis=-1)
+            kth = np.take_along_axis(pv, order[..., below:below + 1], axis=-1)
+            # n_tie distinct picks among the `below` smallest positions
+            pick = g.integers(0, below, size=pv.shape[:2] + (1,))
+            for k in range(1, n_tie):
+                nxt = g.integers(0, below - k, size=pv.shape[:2] + (1,))
+                for col in np.split(np.sort(pick, axis=-1), pick.shape[-1], axis=-1):
+                    nxt += nxt >= col
+                pick = np.concatenate([pick, nxt], axis=-1)
+            dst = np.take_along_axis(order, pick, axis=-1)
+            np.put_along_axis(pv, dst, np.broadcast_to(kth, dst.shape), axis=-1)
+        return p
     if n_tie:
         nb = d_i // bank
         pv = p.reshape(T, nb, bank)
@@ -193,4 +221,6 @@ CONFIGS = {
     "prefill": dict(shape=FULL, T=4096, outlier_frac=0.01),
     "longctx": dict(shape=FULL, T=32768, chunk=4096, outlier_frac=0.01),
     "topk_stress": dict(T=32768, d_i=14336, tie_frac=0.05),
+    # the same with the ties planted on each bank's keep boundary
+    "topk_stress_boundary": dict(T=32768, d_i=14336, tie_frac=0.05, ties="boundary"),
 }
