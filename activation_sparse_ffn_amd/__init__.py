@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "sparse_ffn_packed_size", "sparse_ffn_create", "sparse_ffn_workspace_size",
     "sparse_ffn_forward", "bank_topk", "sparse_ffn_destroy", "sparse_ffn_status_string",
     "sparse_ffn_last_error", "sparse_ffn_set_stage_events", "sparse_ffn_stage_name",
-    "sparse_ffn_backward_workspace_size", "sparse_ffn_backward",
+    "sparse_ffn_backward_workspace_size", "sparse_ffn_backward", "sparse_ffn_forward_noalloc",
 )
 SFFN_STAGES = 5
 SFFN_FLAG_BACKWARD = 1
@@ -98,6 +98,8 @@ def load_library():
     lib.sparse_ffn_backward_workspace_size.restype = S
     lib.sparse_ffn_backward.argtypes = [P, P, P, P, I64, ctypes.c_float, P, P, P, P, P, P, P, P, S, P]
     lib.sparse_ffn_backward.restype = st
+    lib.sparse_ffn_forward_noalloc.argtypes = [P, P, I64, P, P, P, P]
+    lib.sparse_ffn_forward_noalloc.restype = st
     _LIB = lib
     return lib
 

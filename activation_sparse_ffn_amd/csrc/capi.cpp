@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -156,6 +157,54 @@ sffn_status_t hip_status(hipError_t e, const char* what) {
 template <typename P>
 P* at(void* base, size_t off) {
     return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+
+// ---- static scratch of sparse_ffn_forward_noalloc ----------------------------
+// The workspace of a forward, for callers that cannot allocate: one array per
+// GPU, allocated when the library's code object is loaded on that GPU and
+// held until the process ends. 16 MiB covers every path of the full layer
+// (d = 4096, d_i = 14336, rank 448) up to T = 64: the token-gather path needs
+// 14.2 MiB at T = 4, the skinny MFMA path 9.4 MiB at T = 64.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on each GPU (the host-side name `scratch` is a
+// stand-in, never a device address), asked once per device with that device
+// current.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+sffn_status_t scratch_for_stream(hipStream_t s, void** out) {
+    int dev = -1, cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    dev = cur;
+    if (s != nullptr) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(s, &sd);
+        if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SFFN_ERR_UNSUPPORTED, "device %d is beyond the %d the static scratch serves", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & (kAlign - 1)) != 0)
+            return fail(SFFN_ERR_HIP, "the static scratch of device %d has no usable address", dev);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SFFN_OK;
 }
 
 }  // namespace
@@ -323,6 +372,21 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         else he = sffn::launch_mfma_forward(a, s);
     }
     return hip_status(he, "sparse_ffn_forward");
+}
+
+sffn_status_t sparse_ffn_forward_noalloc(sffn_handle_t h, const void* x, int64_t T, void* y,
+                                         uint64_t* mask_out, float* logits_out, void* hip_stream) {
+    if (!h) return fail(SFFN_ERR_INVALID_ARG, "handle is null");
+    if (T < 0) return fail(SFFN_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+    if (T == 0) return SFFN_OK;
+    const size_t need = sparse_ffn_workspace_size(h, T);
+    if (need > kScratchBytes)
+        return fail(SFFN_ERR_WORKSPACE, "T = %lld needs %zu bytes of scratch; the static scratch holds %zu",
+                    (long long)T, need, kScratchBytes);
+    void* ws = nullptr;
+    const sffn_status_t st = scratch_for_stream(static_cast<hipStream_t>(hip_stream), &ws);
+    if (st != SFFN_OK) return st;
+    return sparse_ffn_forward(h, x, T, y, mask_out, logits_out, ws, kScratchBytes, hip_stream);
 }
 
 size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T) {

@@ -145,6 +145,25 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T,
                                  float* logits_out, void* workspace,
                                  size_t ws_bytes, void* hip_stream);
 
+/* sparse_ffn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The scratch is a static array of
+ * 16 MiB per GPU inside the library, allocated when the library's code is
+ * loaded on that GPU and kept until the process ends; it covers every path
+ * of the full layer (d = 4096, d_i = 14336, rank 448) up to T = 64. A call
+ * whose sparse_ffn_workspace_size(h, T) exceeds it returns
+ * SFFN_ERR_WORKSPACE and enqueues nothing. Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams,
+ * different threads) race and must not be issued; calls on one stream are
+ * ordered and safe. The scratch keeps the last call's contents; every byte a
+ * call reads is written earlier in the same call. The first call on a GPU
+ * looks the array's address up (hipGetSymbolAddress on the stream's device);
+ * no call allocates or frees device memory. Arguments and results are those
+ * of sparse_ffn_forward. */
+sffn_status_t sparse_ffn_forward_noalloc(sffn_handle_t h, const void* x, int64_t T,
+                                         void* y, uint64_t* mask_out,
+                                         float* logits_out, void* hip_stream);
+
 /* Bank-wise hard top-k alone (Methodologie > 1. Architectuur, the bank rule):
  *   logits  [T, d_i] fp32 (device)
  *   mask_out [T, d_i/64] uint64 (device): exactly `keep` bits per word
