@@ -72,6 +72,11 @@ def parse():
                          "own workspace), so that one chunk's kernels can fill another's gaps")
     ap.add_argument("--keep", type=int, default=16,
                     help="channels kept per 64-channel bank (64: the dense modes)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the chosen workload alone (a default run adds the batched, prefill, "
+                         "long-context, top-k stress and backward workloads as sub-records)")
+    ap.add_argument("--ties", choices=["random", "boundary"], default="random",
+                    help="topk workload: where the 5%% exact ties per bank are planted")
     ap.add_argument("--gate", choices=["pred", "silu", "amplitude"], default="pred",
                     help="gate of the kept channels: sigmoid of the predictor logit or of u; "
                          "amplitude: the Dense-4x post-hoc baseline (no predictor)")
@@ -138,9 +143,31 @@ def profiled_traffic(kernel):
     return None
 
 
+def host_cpu():
+    """The host the oracle runs on: logical CPUs, the ones this process may
+    use, the CPU model and whether SMT is on."""
+    info = {"nproc": os.cpu_count() or 1}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        info["smt"] = open("/sys/devices/system/cpu/smt/active").read().strip() == "1"
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(layer, T, budget_s, keep=16, gate="pred"):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
+    """The oracle, as it stands, on a bounded sample of the same workload.
+    `cores` is the number of threads the oracle's BLAS calls run on."""
     import oracle as o
     import workloads as wl
     try:
@@ -160,7 +187,7 @@ def cpu_baseline(layer, T, budget_s, keep=16, gate="pred"):
     el = time.perf_counter() - t0
     out = dict(value=n_tok / el, unit="tokens/s", cores=int(cores), kind="oracle",
                sample=f"{n_tok} tokens of the same layer in groups of {chunk}, "
-                      f"{el:.1f} s wall, float64 numpy oracle")
+                      f"{el:.1f} s wall, float64 numpy oracle", **host_cpu())
     # the same on one thread, over a third of the budget
     try:
         from threadpoolctl import threadpool_limits
@@ -221,66 +248,61 @@ def copy_calibration(args):
           flush=True)
 
 
-def topk_stress(args):
+def dev(a):
+    """A numpy array (bf16 bit patterns as uint16, or fp32) as a GPU tensor."""
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def topk_stress(steps, warmup, ties="random"):
     """bank_topk alone on the stress logits: bytes read + mask bytes written."""
     import numpy as np
     import torch
     import activation_sparse_ffn_amd as sffn
     import workloads as wl
-    cfg = wl.CONFIGS["topk_stress"]
+    cfg = wl.CONFIGS["topk_stress" if ties == "random" else "topk_stress_boundary"]
     t0 = time.time()
-    p = torch.from_numpy(wl.make_stress_logits(cfg["T"], cfg["d_i"], seed=0, tie_frac=cfg["tie_frac"])).cuda()
+    p = torch.from_numpy(wl.make_stress_logits(cfg["T"], cfg["d_i"], seed=0, tie_frac=cfg["tie_frac"],
+                                               ties=ties)).cuda()
     T, d_i = p.shape
     mask = torch.empty((T, d_i // 64), dtype=torch.int64, device="cuda")
-    log(f"setup {time.time() - t0:.1f}s")
-    for _ in range(args.warmup):
+    log(f"topk setup {time.time() - t0:.1f}s ({ties} ties)")
+    for _ in range(warmup):
         sffn.bank_topk(p, 16, mask_out=mask)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         sffn.bank_topk(p, 16, mask_out=mask)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = e0.elapsed_time(e1) / steps
     nbytes = p.numel() * 4 + mask.numel() * 8
     gbs = nbytes / (ms * 1e-3) / 1e9
     w = mask.cpu().numpy().view(np.uint64)
     assert (np.bitwise_count(w) == 16).all()
-    print(json.dumps({"metric": "bank_topk stress: 32768 x 14336 fp32 logits, keep 16 of 64",
-                      "value": round(gbs, 1), "unit": "GB/s", "steps": args.steps, "warmup": args.warmup,
-                      "ms_per_step": round(ms, 4), "banks_per_s": round(T * d_i / 64 / (ms * 1e-3), 1),
-                      "bytes_per_step": nbytes,
-                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}), flush=True)
+    del p
+    return {"metric": "bank_topk stress: 32768 x 14336 fp32 logits, keep 16 of 64",
+            "value": round(gbs, 1), "unit": "GB/s", "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 4), "banks_per_s": round(T * d_i / 64 / (ms * 1e-3), 1),
+            "bytes_per_step": nbytes, "ties": f"5% per bank ({ties})",
+            "roofline": {"kernel": "k_bank_topk_lanes", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
-def backward_bench(args):
+def backward_bench(ffns, steps, warmup, keep, gate):
     """One backward pass (soft surrogate through the bank top-k) of a
-    4096-token chunk of the full layer, rotating 2 layers; executed TFLOP/s."""
-    import numpy as np
+    4096-token chunk of the full layer, rotating the given layers (created
+    with for_backward=True); executed TFLOP/s."""
     import torch
-
-    import activation_sparse_ffn_amd as sffn
     import workloads as wl
 
-    T, n_layers = 4096, args.layers or 2
+    T, n_layers = 4096, len(ffns)
     shape = wl.FULL
     d, d_i, r = shape.d, shape.d_i, shape.rank
-
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-    t0 = time.time()
-    ffns = []
-    for li in range(n_layers):
-        L = wl.make_layer(shape, seed=li)
-        # a layer meant for training keeps W_g^T and W_u^T packed
-        ffns.append(sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B), None,
-                                   keep=args.keep, gate=args.gate, for_backward=True))
-        del L
     x = dev(wl.make_tokens(shape, T, seed=1, outlier_frac=0.01))
     gy = dev(wl.make_tokens(shape, T, seed=2))
     masks = []
@@ -289,8 +311,8 @@ def backward_bench(args):
         masks.append(m)
     ws = torch.empty(ffns[0]._lib.sparse_ffn_backward_workspace_size(ffns[0]._h, T), dtype=torch.uint8,
                      device="cuda")
-    log(f"setup {time.time() - t0:.1f}s, backward workspace {ws.numel() / 2**30:.2f} GiB")
-    K, W = max(1, min(args.steps, 64)), max(1, min(args.warmup, 8))
+    log(f"backward workspace {ws.numel() / 2**30:.2f} GiB")
+    K, W = max(1, min(steps, 64)), max(1, min(warmup, 8))
     for i in range(W):
         ffns[i % n_layers].backward(x, gy, masks[i % n_layers], workspace=ws)
     torch.cuda.synchronize()
@@ -305,76 +327,41 @@ def backward_bench(args):
     fl = 2 * T * (d * r + r * d_i + 2 * d * d_i + d * d_i + d * d_i + 2 * d * d_i
                   + d_i * r + d_i * r + r * d + d * r + 2 * d * d_i)
     tf = fl / (ms * 1e-3) / 1e12
-    print(json.dumps({"metric": "sparse-FFN backward (soft surrogate top-k), 4096-token chunk",
-                      "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-                      "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
-                      "config": {"workload": f"backward: {T} tokens, d={d}, d_i={d_i}, rank={r}, "
-                                             f"keep {args.keep} of 64, gate {args.gate}, tau 1",
-                                 "layers_rotated": n_layers},
-                      "executed_flops": fl,
-                      "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}), flush=True)
+    del ws
+    return {"metric": "sparse-FFN backward (soft surrogate top-k), 4096-token chunk",
+            "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "steps": K,
+            "warmup": W, "ms_per_step": round(ms, 4), "dtype": "bf16",
+            "config": {"workload": f"backward: {T} tokens, d={d}, d_i={d_i}, rank={r}, "
+                                   f"keep {keep} of 64, gate {gate}, tau 1",
+                       "layers_rotated": n_layers},
+            "executed_flops": fl,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path "
-              "(the layer would shard by tokens, with no exchange, or by banks, with one "
-              "all-reduce of y).", file=sys.stderr)
-        sys.exit(2)
+def forward_bench(name, ffns, shape, K, W, keep, gate, graph=True, n_streams=1):
+    """Time K steps of workload `name` (decode, batched, prefill, long) over
+    the given layers, then time every kernel stage with start/stop events;
+    returns the record (without the CPU baseline)."""
     import numpy as np
     import torch
-
     import activation_sparse_ffn_amd as sffn
     import workloads as wl
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    if args.workload == "copy":
-        copy_calibration(args)
-        return
-    if args.workload == "topk":
-        topk_stress(args)
-        return
-    if args.workload == "backward":
-        backward_bench(args)
-        return
-    cfg = WORKLOADS[args.workload]
+    cfg = WORKLOADS[name]
     T = cfg["T"]
-    n_layers = args.layers or cfg["layers"]
-    shape = dataclasses.replace(wl.FULL, keep=args.keep)
-    K, W = args.steps, args.warmup
-
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-    # ---- layers and tokens -------------------------------------------------
+    n_layers = len(ffns)
     t0 = time.time()
-    ffns, layer0 = [], None
-    for li in range(n_layers):
-        L = wl.make_layer(shape, seed=li, bias_var=0.5 if cfg["bias"] else None)
-        ffns.append(sffn.SparseFFN(dev(L.W_g), dev(L.W_u), dev(L.W_d), dev(L.A), dev(L.B),
-                                   dev(L.bias) if cfg["bias"] else None, keep=args.keep, gate=args.gate))
-        if li == 0:
-            layer0 = L
-        del L
-        torch.cuda.empty_cache()
-    n_x = 64 if T == 1 else (16 if T <= 32 else 2)
-    xs = [dev(wl.make_tokens(shape, T, seed=10_000 + i, outlier_frac=cfg["outliers"]))
-          for i in range(n_x)]
+    n_x = 64 if T == 1 else (16 if T <= 32 else (2 if T <= 4096 else 1))
+    xs = [dev(wl.make_tokens(shape, T, seed=10_000 + i, outlier_frac=cfg["outliers"])) for i in range(n_x)]
     ys = [torch.empty_like(x) for x in xs]
     chunk = cfg.get("chunk", T)
     n_chunks = T // chunk
-    n_streams = max(1, min(args.streams, n_chunks))
+    n_streams = max(1, min(n_streams, n_chunks))
     wss = [torch.empty(ffns[0].workspace_size(chunk), dtype=torch.uint8, device="cuda")
            for _ in range(n_streams)]
     masks = [torch.empty((T, shape.n_banks), dtype=torch.int64, device="cuda") for _ in range(n_x)]
-    log(f"setup {time.time() - t0:.1f}s: {n_layers} layers, {n_x} token batches of T={T}"
+    log(f"{name}: tokens {time.time() - t0:.1f}s: {n_layers} layers, {n_x} token batches of T={T}"
         + (f" in {n_chunks} chunks of {chunk} over {n_streams} stream(s)" if n_chunks > 1 else ""))
 
     G = n_x * n_layers // np.gcd(n_x, n_layers)     # steps per graph: every (x, layer) pair once
@@ -405,13 +392,13 @@ def main():
             step(i)
     torch.cuda.synchronize()
 
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
             for i in range(G):
                 step(i)
-        graph.replay()
+        g.replay()
         torch.cuda.synchronize()
         # the graph reproduces eager results bit for bit
         y_graph = [y.clone() for y in ys]
@@ -421,15 +408,16 @@ def main():
         torch.cuda.synchronize()
         for a, b in zip(y_graph, ys):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "graph replay differs"
+        del y_graph
 
     # ---- timed region -------------------------------------------------------
-    reps, rem = divmod(K, G) if graph is not None else (0, K)
+    reps, rem = divmod(K, G) if g is not None else (0, K)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         e0.record(stream)
         for _ in range(reps):
-            graph.replay()
+            g.replay()
         for i in range(rem):
             step(i)
         e1.record(stream)
@@ -437,21 +425,22 @@ def main():
     ms = e0.elapsed_time(e1)
     ms_per_step = ms / K
     tokens_per_s = T * K / (ms / 1e3)
-    log(f"timed {K} steps: {ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.1f} tokens/s")
+    log(f"{name}: timed {K} steps: {ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.1f} tokens/s")
 
     # ---- union of kept channels (batched / prefill bytes) -------------------
     union_frac = None
     if T > 1:
         fr = []
         for m in masks:
-            w = m.cpu().numpy().view(np.uint64)
-            fr.append(np.bitwise_count(np.bitwise_or.reduce(w, axis=0)).sum() / shape.d_i)
+            w = m.cpu().numpy().view(np.uint64).reshape(-1, chunk, shape.n_banks)
+            fr.append(np.mean([np.bitwise_count(np.bitwise_or.reduce(c, axis=0)).sum() / shape.d_i for c in w]))
         union_frac = float(np.mean(fr))
-    alg = algorithmic(args.workload, shape, T, union_frac, args.gate)
+    alg = algorithmic(name, shape, chunk if n_chunks > 1 else T, union_frac, gate)
     if n_chunks > 1:
         # every chunk streams the weights of its own union again
-        for key in ("pred", "gateup", "down", "bytes"):
-            alg[key] *= n_chunks
+        for key in ("pred", "gateup", "down", "bytes", "flops", "executed_flops"):
+            if key in alg:
+                alg[key] *= n_chunks
 
     # ---- per-stage durations (kernel start/stop events) ---------------------
     n_ev = 2 * sffn.SFFN_STAGES
@@ -474,10 +463,11 @@ def main():
     stage_us = stage_ms / n_prof * 1e3
     names = ffns[0].stage_names(chunk)
     stages = {n: round(float(u), 3) for n, u in zip(names, stage_us) if n != "none"}
-    log(f"stages (us): {stages}")
+    log(f"{name}: stages (us): {stages}")
 
-    # ---- roofline of the dominant kernel ------------------------------------
-    if args.workload == "decode":
+    # ---- roofline of the dominant kernel, and of the whole step --------------
+    step_s = ms_per_step * 1e-3
+    if name == "decode":
         if "bank_fused" in names:
             dom, kname = "bank_fused", "k_bank_fused"
             nbytes = alg["pred_b"] + alg["gateup"] + alg["down"]
@@ -487,24 +477,45 @@ def main():
             nbytes = alg["gateup"]
         dur_s = stage_us[names.index(dom)] * 1e-6
         achieved = nbytes / dur_s / 1e9
+        traffic = profiled_traffic(kname) if (keep == 16 and gate == "pred") else None
         roof = dict(kernel=kname, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=profiled_traffic(kname),
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     bytes_per_launch=nbytes, avg_us=round(float(stage_us[names.index(dom)]), 3))
+        if traffic is not None:
+            roof["traffic_from"] = "profiles/decode_T1_hbm_counters.md (rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE)"
+        gbs = alg["bytes"] / step_s / 1e9
+        step_roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), bytes_per_step=alg["bytes"])
+    elif name == "batched":
+        # a T = 32 batch is bound by streaming the union's weight rows
+        dom = next(n for n in names if n.startswith("gateup"))
+        dur_s = stage_us[names.index(dom)] * 1e-6
+        gb = alg["gateup"] / dur_s / 1e9
+        roof = dict(kernel="k_skinny<SK_GATEUP>", bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(gb / HBM_PEAK_GBS, 4), traffic=None, bytes_per_launch=alg["gateup"],
+                    avg_us=round(float(stage_us[names.index(dom)]), 3))
+        gbs = alg["bytes"] / step_s / 1e9
+        step_roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), bytes_per_step=alg["bytes"])
     else:
         dom = next(n for n in names if n.startswith("gateup"))
         dur_s = stage_us[names.index(dom)] * 1e-6
         fl = 2 * chunk * 2 * shape.d_i * shape.d    # executed per launch: dense gate and up
         achieved = fl / dur_s / 1e12
-        roof = dict(kernel="k_gemm<EPI_GATEUP>", bound="mfma", achieved=round(achieved, 1),
+        roof = dict(kernel="k_gemm256<EPI_GATEUP>", bound="mfma", achieved=round(achieved, 1),
                     peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4),
-                    traffic=None, flops_per_launch=fl,
-                    avg_us=round(float(stage_us[names.index(dom)]), 3))
-        if args.workload == "batched":
-            # a T = 32 batch is bound by streaming the union's weight rows
-            gb = alg["gateup"] / dur_s / 1e9
-            roof.update(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(gb / HBM_PEAK_GBS, 4), bytes_per_launch=alg["gateup"])
-            roof.pop("flops_per_launch")
+                    traffic=None, flops_per_launch=fl, avg_us=round(float(stage_us[names.index(dom)]), 3))
+        if "down_gemm" in names:
+            dd = stage_us[names.index("down_gemm")] * 1e-6
+            fd = 2 * chunk * shape.d_i * shape.d
+            roof["down_gemm"] = dict(avg_us=round(dd * 1e6, 3), achieved=round(fd / dd / 1e12, 1),
+                                     frac=round(fd / dd / 1e12 / BF16_PEAK_TFLOPS, 4))
+        ex = alg["executed_flops"] / step_s / 1e12
+        al = alg["flops"] / step_s / 1e12
+        step_roof = dict(bound="mfma", achieved=round(ex, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                         frac=round(ex / BF16_PEAK_TFLOPS, 4), executed_flops_per_step=alg["executed_flops"],
+                         algorithmic=round(al, 1), algorithmic_frac=round(al / BF16_PEAK_TFLOPS, 4),
+                         algorithmic_flops_per_step=alg["flops"])
 
     out = {
         "metric": METRIC,
@@ -520,22 +531,115 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0, 1/fan_in) weights, N(0, 1) tokens)",
         "config": {
-            "workload": f"{args.workload}: {T} token(s) per step, d=4096, d_i=14336, rank=448, "
-                        f"keep {args.keep} of 64 per bank, gate {args.gate}, {n_layers} layers rotated",
-            "tokens_per_step": T, "layers_rotated": n_layers, "graph": graph is not None,
+            "workload": f"{name}: {T} token(s) per step, d=4096, d_i=14336, rank=448, "
+                        f"keep {keep} of 64 per bank, gate {gate}, {n_layers} layers rotated"
+                        + (", predictor bias N(0, 0.5)" if cfg["bias"] else "")
+                        + (", 1% outlier feature columns x20" if cfg["outliers"] else ""),
+            "tokens_per_step": T, "layers_rotated": n_layers, "graph": g is not None,
             **({"chunk": chunk, "streams": n_streams} if n_chunks > 1 else {}),
         },
-        "step_hbm_gbs": round(alg["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": alg["bytes"],
         "stages_us": stages,
         "roofline": roof,
+        "step_roofline": step_roof,
     }
     if union_frac is not None:
         out["union_frac"] = round(union_frac, 4)
-        out["executed_tflops"] = round(alg["executed_flops"] / (ms_per_step * 1e-3) / 1e12, 1)
+    del xs, ys, wss, masks
+    return out
+
+
+def make_layers(shape, n, keep, gate, bias_layers=0, backward_layers=0):
+    """n layers drawn with seeds 0 .. n-1 and packed for the GPU; the first
+    `bias_layers` also packed with their predictor bias, the first
+    `backward_layers` also packed for the backward pass. Returns the three
+    lists and layer 0's host arrays (for the CPU baseline)."""
+    import torch
+    import activation_sparse_ffn_amd as sffn
+    import workloads as wl
+    plain, biased, bwd, layer0 = [], [], [], None
+    for li in range(n):
+        L = wl.make_layer(shape, seed=li, bias_var=0.5)
+        W = [dev(a) for a in (L.W_g, L.W_u, L.W_d, L.A, L.B)]
+        plain.append(sffn.SparseFFN(*W, None, keep=keep, gate=gate))
+        if li < bias_layers:
+            biased.append(sffn.SparseFFN(*W, dev(L.bias), keep=keep, gate=gate))
+        if li < backward_layers and gate != "amplitude":
+            bwd.append(sffn.SparseFFN(*W, None, keep=keep, gate=gate, for_backward=True))
+        if li == 0:
+            layer0 = wl.Layer(L.shape, L.A, L.B, L.W_g, L.W_u, L.W_d, None)
+        del L, W
+        torch.cuda.empty_cache()
+    return plain, biased, bwd, layer0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the layer would shard by tokens, with no exchange, or by banks, with one "
+              "all-reduce of y).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.workload == "copy":
+        copy_calibration(args)
+        return
+    K, W = args.steps, args.warmup
+    if args.workload == "topk":
+        print(json.dumps(topk_stress(K, W, args.ties)), flush=True)
+        return
+    shape = dataclasses.replace(wl.FULL, keep=args.keep)
+    if args.workload == "backward":
+        _, _, bwd, _ = make_layers(shape, args.layers or 2, args.keep, args.gate, backward_layers=args.layers or 2)
+        rec = backward_bench(bwd, K, W, args.keep, args.gate)
+        rec.update(n_gpus=1, higher_is_better=True)
+        print(json.dumps(rec), flush=True)
+        return
+
+    # the headline workload, and in a default run the others as sub-records
+    subs = [] if args.only else ["batched", "prefill", "long", "topk", "backward"]
+    n_layers = args.layers or WORKLOADS[args.workload]["layers"]
+    want_bias = WORKLOADS[args.workload]["bias"]
+    n_bias = max(n_layers if want_bias else 0, WORKLOADS["batched"]["layers"] if "batched" in subs else 0)
+    n_bwd = 2 if "backward" in subs else 0
+    t0 = time.time()
+    plain, biased, bwd, layer0 = make_layers(shape, max(n_layers, 2), args.keep, args.gate,
+                                             bias_layers=n_bias, backward_layers=n_bwd)
+    log(f"setup {time.time() - t0:.1f}s: {len(plain)} layers (+{len(biased)} with bias, +{len(bwd)} for backward)")
+    head = biased[:n_layers] if want_bias else plain[:n_layers]
+    out = forward_bench(args.workload, head, shape, K, W, args.keep, args.gate, graph=not args.no_graph,
+                        n_streams=args.streams)
+    sub = {}
+    Ks, Ws = max(K, 8), max(W, 2)
+    for name in subs:
+        if name == args.workload:
+            continue
+        t1 = time.time()
+        if name == "topk":
+            sub[name] = topk_stress(Ks, Ws)
+        elif name == "backward":
+            sub[name] = backward_bench(bwd, Ks, Ws, args.keep, args.gate)
+        else:
+            layers = biased[:WORKLOADS[name]["layers"]] if WORKLOADS[name]["bias"] else plain[:WORKLOADS[name]["layers"]]
+            rec = forward_bench(name, layers, shape, Ks, Ws, args.keep, args.gate, graph=not args.no_graph)
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "dtype", "data"):
+                rec.pop(k, None)
+            sub[name] = rec
+        sub[name]["wall_s"] = round(time.time() - t1, 1)
+        torch.cuda.empty_cache()
+    if sub:
+        out["sub"] = sub
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
-        out["cpu_baseline"] = cpu_baseline(layer0, T, args.cpu_seconds, args.keep, args.gate)
+        out["cpu_baseline"] = cpu_baseline(layer0, WORKLOADS[args.workload]["T"], args.cpu_seconds, args.keep,
+                                           args.gate)
     print(json.dumps(out), flush=True)
 
 
