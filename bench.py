@@ -365,7 +365,7 @@ def forward_bench(name, ffns, shape, K, W, keep, gate, graph=True, n_streams=1):
         + (f" in {n_chunks} chunks of {chunk} over {n_streams} stream(s)" if n_chunks > 1 else ""))
 
     G = n_x * n_layers // np.gcd(n_x, n_layers)     # steps per graph: every (x, layer) pair once
-    G = min(G, 64)
+    G = min(G, 64, K)                               # K <= 64: the timed region is one replay
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
