@@ -48,6 +48,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_size(sffn_dtype_t dt) { return dt == SFFN_BF16 ? 2 : 4; }
 
+template <typename Enum>
+int as_int(const Enum& e) {
+    static_assert(sizeof(Enum) == sizeof(int), "enums of the C ABI are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 sffn_status_t check_config(const sffn_config_t* c) {
     if (!c) return fail(SFFN_ERR_INVALID_ARG, "config is null");
     if (c->d <= 0 || c->d_i <= 0 || c->rank <= 0)
@@ -61,10 +69,13 @@ sffn_status_t check_config(const sffn_config_t* c) {
     if (c->d % 64 != 0) return fail(SFFN_ERR_INVALID_ARG, "d must be a multiple of 64 (got %d)", c->d);
     if (c->rank % 32 != 0)
         return fail(SFFN_ERR_INVALID_ARG, "rank must be a multiple of 32 (got %d)", c->rank);
-    if (c->dtype != SFFN_F32 && c->dtype != SFFN_BF16)
-        return fail(SFFN_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
-    if (c->gate != SFFN_GATE_PREDICTOR && c->gate != SFFN_GATE_SILU && c->gate != SFFN_GATE_AMPLITUDE)
-        return fail(SFFN_ERR_INVALID_ARG, "unknown gate %d", (int)c->gate);
+    // the enum fields come from C callers as plain ints: read them as ints
+    // (an out-of-range value read as a C++ enum is undefined behaviour)
+    const int dtype = as_int(c->dtype), gate = as_int(c->gate);
+    if (dtype != SFFN_F32 && dtype != SFFN_BF16)
+        return fail(SFFN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (gate != SFFN_GATE_PREDICTOR && gate != SFFN_GATE_SILU && gate != SFFN_GATE_AMPLITUDE)
+        return fail(SFFN_ERR_INVALID_ARG, "unknown gate %d", gate);
     if (c->flags & ~SFFN_FLAG_BACKWARD) return fail(SFFN_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     return SFFN_OK;
 }
@@ -148,6 +159,18 @@ WsMfma ws_mfma(const sffn_config_t& c, int64_t T) {
     w.total = off;
     return w;
 }
+
+// Token counts a forward accepts: every launch's grid must fit in 31 bits,
+// and T is bounded first so that none of the size products can overflow.
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+bool tokens_fit(const sffn_config_t& c, int64_t T) {
+    if (T > kMaxTokens) return false;
+    const int64_t nb = c.d_i / 64, ds = nb * c.keep;
+    const int64_t biggest = std::max(T * (int64_t)c.d_i, T * ds * 2);
+    return biggest / 4 < kMaxGrid && T * nb * 8 < kMaxGrid;
+}
+// the backward pass: T tokens padded to 64, transposed operands of T columns
+constexpr int64_t kMaxBackwardTokens = (int64_t)1 << 24;
 
 sffn_status_t hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return SFFN_OK;
@@ -285,7 +308,7 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* w_gate, co
 }
 
 size_t sparse_ffn_workspace_size(sffn_handle_t h, int64_t T) {
-    if (!h || T <= 0) return 0;
+    if (!h || T <= 0 || !tokens_fit(h->cfg, T)) return 0;
     return use_gather(h->cfg, T) ? ws_gather(h->cfg, T).total : ws_mfma(h->cfg, T).total;
 }
 
@@ -304,11 +327,7 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
     if (!workspace) return fail(SFFN_ERR_INVALID_ARG, "workspace is null");
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
         return fail(SFFN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    const int64_t nb = c.d_i / 64, ds = nb * c.keep;
-    // every launch's grid must fit in 31 bits
-    const int64_t biggest = T * (int64_t)c.d_i > T * ds * 2 ? T * (int64_t)c.d_i : T * ds * 2;
-    if (biggest / 4 >= kMaxGrid || T * nb * 8 >= kMaxGrid)
-        return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
+    if (!tokens_fit(c, T)) return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
     const size_t need = sparse_ffn_workspace_size(h, T);
     if (ws_bytes < need)
         return fail(SFFN_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed for T = %lld", ws_bytes,
@@ -379,6 +398,8 @@ sffn_status_t sparse_ffn_forward_noalloc(sffn_handle_t h, const void* x, int64_t
     if (!h) return fail(SFFN_ERR_INVALID_ARG, "handle is null");
     if (T < 0) return fail(SFFN_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
     if (T == 0) return SFFN_OK;
+    if (!tokens_fit(h->cfg, T))
+        return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
     const size_t need = sparse_ffn_workspace_size(h, T);
     if (need > kScratchBytes)
         return fail(SFFN_ERR_WORKSPACE, "T = %lld needs %zu bytes of scratch; the static scratch holds %zu",
@@ -390,7 +411,7 @@ sffn_status_t sparse_ffn_forward_noalloc(sffn_handle_t h, const void* x, int64_t
 }
 
 size_t sparse_ffn_backward_workspace_size(sffn_handle_t h, int64_t T) {
-    if (!h || T <= 0) return 0;
+    if (!h || T <= 0 || T > kMaxBackwardTokens || T * h->cfg.d_i / 4 >= kMaxGrid) return 0;
     return sffn::backward_workspace_bytes(T, h->cfg.d, h->cfg.d_i, h->cfg.rank,
                                           (h->cfg.flags & SFFN_FLAG_BACKWARD) != 0);
 }
@@ -432,7 +453,7 @@ sffn_status_t sparse_ffn_backward(sffn_handle_t h, const void* x, const void* g_
     if (!workspace) return fail(SFFN_ERR_INVALID_ARG, "workspace is null");
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
         return fail(SFFN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    if (T * di / 4 >= kMaxGrid || T > (int64_t)1 << 24)
+    if (T > kMaxBackwardTokens || T * di / 4 >= kMaxGrid)
         return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
     const size_t need = sparse_ffn_backward_workspace_size(h, T);
     if (ws_bytes < need)
@@ -469,6 +490,7 @@ sffn_status_t bank_topk(const float* logits, int64_t T, int32_t d_i, int32_t kee
         return fail(SFFN_ERR_INVALID_ARG, "d_i must be a positive multiple of 64, <= 65536 (got %d)", d_i);
     if (keep < 1 || keep > 64) return fail(SFFN_ERR_INVALID_ARG, "keep must lie in [1, 64] (got %d)", keep);
     if (T == 0) return SFFN_OK;
+    if (T > kMaxTokens) return fail(SFFN_ERR_UNSUPPORTED, "T = %lld is too large for one call", (long long)T);
     if (!logits || !mask_out) return fail(SFFN_ERR_INVALID_ARG, "logits and mask_out must not be null");
     if (!aligned16(logits) || !aligned16(mask_out) || (idx_out && !aligned16(idx_out)))
         return fail(SFFN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
@@ -526,8 +548,8 @@ const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
 
 void sparse_ffn_destroy(sffn_handle_t h) { delete h; }
 
-const char* sparse_ffn_status_string(sffn_status_t s) {
-    switch (s) {
+const char* sparse_ffn_status_string(sffn_status_t status) {
+    switch (as_int(status)) {
         case SFFN_OK: return "ok";
         case SFFN_ERR_INVALID_ARG: return "invalid argument";
         case SFFN_ERR_UNSUPPORTED: return "unsupported";
