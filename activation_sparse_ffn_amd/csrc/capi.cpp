@@ -80,8 +80,11 @@ sffn_status_t check_config(const sffn_config_t* c) {
     return SFFN_OK;
 }
 
+// The packed weights: A, B, W_g, W_u, W_d^T (the only copy of the down
+// projection: decode gathers its rows, the MFMA paths read it K-major), the
+// bias, and with SFFN_FLAG_BACKWARD W_g^T and W_u^T.
 struct PackedLayout {
-    size_t A, B, Wg, Wu, Wd, WdT, bias, WgT, WuT, total;   // WgT, WuT: SFFN_FLAG_BACKWARD only
+    size_t A, B, Wg, Wu, WdT, bias, WgT, WuT, total;   // WgT, WuT: SFFN_FLAG_BACKWARD only
 };
 
 PackedLayout packed_layout(const sffn_config_t& c) {
@@ -93,7 +96,6 @@ PackedLayout packed_layout(const sffn_config_t& c) {
     L.B = off;    off += align_up(di * r * e);
     L.Wg = off;   off += align_up(di * d * e);
     L.Wu = off;   off += align_up(di * d * e);
-    L.Wd = off;   off += align_up(d * di * e);
     L.WdT = off;  off += align_up(di * d * e);
     L.bias = off; off += align_up(di * 4);
     L.WgT = L.WuT = 0;
@@ -285,7 +287,6 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* w_gate, co
     if (pred_b) cp(L.B, pred_b, di * r * e);
     cp(L.Wg, w_gate, di * d * e);
     cp(L.Wu, w_up, di * d * e);
-    cp(L.Wd, w_down, d * di * e);
     if (pred_bias) cp(L.bias, pred_bias, di * 4);
     if (he == hipSuccess) he = sffn::launch_transpose(dt, w_down, at<char>(packed, L.WdT), cfg->d, cfg->d_i, s);
     if (cfg->flags & SFFN_FLAG_BACKWARD) {
@@ -370,7 +371,7 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.x = static_cast<const uint16_t*>(x);
         a.A = at<const uint16_t>(pk, L.A); a.B = at<const uint16_t>(pk, L.B); a.bias = bias;
         a.W_g = at<const uint16_t>(pk, L.Wg); a.W_u = at<const uint16_t>(pk, L.Wu);
-        a.W_d = at<const uint16_t>(pk, L.Wd);
+        a.W_dT = at<const uint16_t>(pk, L.WdT);
         a.y = static_cast<uint16_t*>(y);
         a.z = at<uint16_t>(workspace, w.z);
         a.logits = logits_out ? logits_out : at<float>(workspace, w.logits);

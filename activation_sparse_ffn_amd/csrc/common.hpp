@@ -93,6 +93,44 @@ template <> struct Raw<float> {
 };
 
 // ---------------------------------------------------------------------------
+// K-major operands: fragments of v_mfma_f32_32x32x16_bf16 from a [K][N] tile
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// An LDS slab of 64 K-rows of ROW_BYTES bytes (N contiguous, bf16), whose
+// 16-byte chunk c of K-row r sits at slot kmajor_slot<ROW_BYTES>(r, c):
+// c ^ (4 (r & 3)) for rows of 256 bytes or more, c ^ (4 ((r >> 1) & 1)) for
+// 128-byte rows (eight chunks). The MFMA wants
+// eight consecutive K of one column per lane (lane l: column col0 + l % 32,
+// K 16 s + 8 (l >> 5) .. + 7). ds_read_b64_tr_b16 gathers that from rows:
+// within each group of 16 lanes, lane i names the 8 bytes at K-row
+// k + (i >> 2), columns n + 4 (i & 3) .. + 3, and lane j receives element
+// j & 3 of the reads of lanes (j >> 2) + 4 e, e = 0..3, i.e. column n + j at
+// K-rows k .. k + 3. Two such reads (K-rows + 0 and + 4) give the fragment.
+// A group's 16 addresses cover 4 K-rows x 32 bytes; the swizzle puts the 4
+// rows on disjoint LDS banks.
+template <int ROW_BYTES>
+__device__ __forceinline__ int kmajor_slot(int r, int c) {
+    static_assert(ROW_BYTES == 128 || ROW_BYTES % 256 == 0, "rows of 128 bytes or whole 256-byte windows");
+    return ROW_BYTES == 128 ? c ^ (4 * ((r >> 1) & 1)) : c ^ (4 * (r & 3));
+}
+template <int ROW_BYTES>
+__device__ __forceinline__ bf16x8 kmajor_frag(const char* slab, int col0, int s, int lane) {
+    const int i16 = lane & 15, g = lane >> 4;
+    const int col = col0 + 16 * (g & 1) + 4 * (i16 & 3);
+    const int kr = 16 * s + 8 * (g >> 1) + (i16 >> 2);
+    // the slot depends on kr & 3 only, which K-row kr + 4 shares
+    const int off = (kmajor_slot<ROW_BYTES>(kr, col >> 3) << 4) + (col & 7) * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(slab + kr * ROW_BYTES + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(slab + (kr + 4) * ROW_BYTES + off));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
 // wave reductions
 // ---------------------------------------------------------------------------
 

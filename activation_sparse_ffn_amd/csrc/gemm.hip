@@ -11,10 +11,14 @@
 //   P = Z B^T + bias (fp32)         k_gemm<EPI_F32_BIAS>
 //   mask = bank top-k of P          k_bank_topk
 //   H = select(m, s * U * V, 0)     k_gemm<EPI_GATEUP>, U = X W_g^T, V = X W_u^T
-//   Y = bf16(H W_d^T)               k_gemm<EPI_BF16>
+//   Y = bf16(H W_d^T)               k_gemm256 / k_gemm <EPI_BF16, K-major W_d^T>
 //
-// Every GEMM is C[M, N] = A[M, K] B[N, K]^T with both operands K-contiguous
-// bf16 and fp32 accumulation on v_mfma_f32_32x32x16_bf16.
+// Every GEMM is C[M, N] = A[M, K] B[N, K]^T with A K-contiguous bf16 and
+// fp32 accumulation on v_mfma_f32_32x32x16_bf16. B is K-contiguous as well,
+// except in the down projection (KMAJOR): there B is W_d^T [K = d_i][N = d],
+// the layout the decode path gathers rows from, so the layer keeps one copy
+// of W_d; its slabs land in LDS row for row and the fragments come out
+// through transposed LDS reads (kmajor_frag).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -65,9 +69,10 @@ constexpr int SLAB128 = BM * TKD * 2;    // one 128-row slab: 16 KB
 // unrolled by two), fragment reads interleaved one per MFMA with the
 // sub-step before, and the barrier before each step's last sub-step. Else
 // the register-staged loop with 32-wide K steps.
-template <int EPI, bool DMA>
+template <int EPI, bool DMA, bool KMAJOR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_TOPK ? 2 : 1))) void k_gemm(const GemmParams p) {
     constexpr int NB = (EPI == EPI_GATEUP || EPI == EPI_UV) ? 2 : 1;
+    static_assert(!KMAJOR || (DMA && EPI == EPI_BF16), "a K-major B only for the plain bf16 GEMM, LDS-direct");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,11 +128,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
             const int gch = fs ^ slab_swz(r);
             const int64_t m = m0 + r;
             asrc[i] = p.A + (m < p.M ? m : 0) * p.K + kb + 8 * gch;
-            const int n = n0 + r;
-            const int64_t nr = n < p.N ? n : 0;
-            bsrc[0][i] = p.B0 + nr * p.K + kb + 8 * gch;
-            if constexpr (NB == 2) bsrc[1][i] = p.B1 + nr * p.K + kb + 8 * gch;
+            if constexpr (KMAJOR) {
+                // K-major B: chunk c = tid + 256 i of the slab is K-row c / 16,
+                // slot c % 16, holding chunk (c % 16) ^ (4 (row & 3)) of the
+                // row's 128 columns; columns past N read column 0 (never stored)
+                const int kr = (tid >> 4) + 16 * i;
+                const int col = n0 + 8 * kmajor_slot<BN * 2>(kr, tid & 15);
+                bsrc[0][i] = p.B0 + (size_t)(kb + kr) * p.N + (col < p.N ? col : 0);
+            } else {
+                const int n = n0 + r;
+                const int64_t nr = n < p.N ? n : 0;
+                bsrc[0][i] = p.B0 + nr * p.K + kb + 8 * gch;
+                if constexpr (NB == 2) bsrc[1][i] = p.B1 + nr * p.K + kb + 8 * gch;
+            }
         }
+        const size_t bstep = KMAJOR ? (size_t)p.N : 1;     // B elements per unit of K
         auto fetch = [&](int k0, char* dst) {
             char* wbase = dst + wv * (kWave * 16);
 #pragma unroll
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     __builtin_amdgcn_global_load_lds(
-                        (const __attribute__((address_space(1))) void*)(bsrc[b][i] + k0),
+                        (const __attribute__((address_space(1))) void*)(bsrc[b][i] + k0 * bstep),
                         (__attribute__((address_space(3))) void*)(wbase + (1 + b) * SLAB128 + i * 4096), 16, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -150,22 +165,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    bfr[b][j] = *reinterpret_cast<const bf16x8*>(S + (1 + b) * SLAB128 +
-                                                                  slab_off(wn * 64 + j * 32 + r32, gch));
+                for (int j = 0; j < 2; ++j) {
+                    if constexpr (KMAJOR)
+                        bfr[b][j] = kmajor_frag<BN * 2>(S + (1 + b) * SLAB128, wn * 64 + j * 32, sub, lane);
+                    else
+                        bfr[b][j] = *reinterpret_cast<const bf16x8*>(S + (1 + b) * SLAB128 +
+                                                                      slab_off(wn * 64 + j * 32 + r32, gch));
+                }
         };
         auto landed = [&]() {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };
         auto interleave = [&]() {
-            constexpr int R = 2 + 2 * NB, M = 4 * NB;
+            // LDS reads of a sub-step (a K-major B fragment takes two) and MFMAs
+            constexpr int R = 2 + (KMAJOR ? 4 : 2) * NB, M = 4 * NB;
+            constexpr int P = R < M ? R : M;
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
+            for (int i = 0; i < P; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            if constexpr (M > R) __builtin_amdgcn_sched_group_barrier(0x008, M - R, 0);
+            if constexpr (M > P) __builtin_amdgcn_sched_group_barrier(0x008, M - P, 0);
+            if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
             __builtin_amdgcn_sched_barrier(0);
         };
         const int kt_n = kn / TKD;
@@ -380,8 +402,9 @@ constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
 
 
-template <int EPI, int WN>
+template <int EPI, int WN, bool KMAJOR = false>
 __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
+    static_assert(!KMAJOR || EPI == EPI_BF16, "a K-major B only for the plain bf16 GEMM");
     // WN waves along N (2 or 4), 2 along M: each wave owns 128 x (256 / WN) of C
     constexpr bool GU = EPI == EPI_GATEUP || EPI == EPI_AMP || EPI == EPI_UV;   // B = [W_g, W_u] blocks
     constexpr int NT = 128 * WN;                     // threads
@@ -429,6 +452,15 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
             const int gch = fs ^ slab_swz(r);
             const int64_t m = mb + r;
             asrc[i] = p.A + (m < p.M ? m : 0) * p.K + 8 * gch;
+            if constexpr (KMAJOR) {
+                // K-major B: chunk c = tid + NT i of the slab is K-row c / 32,
+                // slot c % 32, holding chunk (c % 32) ^ (4 (row & 3)) of the
+                // row's 256 columns; columns past N read column 0 (never stored)
+                const int kr = (tid >> 5) + (NT / 32) * i;
+                const int col = nb0 + 8 * kmajor_slot<TN * 2>(kr, tid & 31);
+                bsrc[i] = p.B0 + (size_t)kr * p.N + (col < p.N ? col : 0);
+                continue;
+            }
             int n;
             const uint16_t* base;
             if constexpr (GU) {
@@ -442,6 +474,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
             bsrc[i] = base + (size_t)(n < p.N ? n : 0) * p.K + 8 * gch;
         }
     };
+    const size_t bstep = KMAJOR ? (size_t)p.N : 1;     // B elements per unit of K
     // gate/up with gate tiles: the 256 x 128 fp16 gate tile of an output block
     // is one contiguous 64 KB block
     auto gate_tile = [&](int mtile, int ntile) -> const uint16_t* {
@@ -460,8 +493,12 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         for (int i = 0; i < 4; ++i)
             af[i] = *reinterpret_cast<const bf16x8*>(As + slab_off(wm * 128 + i * 32 + r32, gch));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * WNC + j * 32 + r32, gch));
+        for (int j = 0; j < NJ; ++j) {
+            if constexpr (KMAJOR)
+                bfr[j] = kmajor_frag<TN * 2>(Bs, wn * WNC + j * 32, s, lane);
+            else
+                bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + slab_off(wn * WNC + j * 32 + r32, gch));
+        }
     };
     auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NJ]) {
 #pragma unroll
@@ -486,7 +523,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
                 (const __attribute__((address_space(1))) void*)(asrc[i] + k0),
                 (__attribute__((address_space(3))) void*)(wbase + i * NT * 16), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(bsrc[i] + k0),
+                (const __attribute__((address_space(1))) void*)(bsrc[i] + k0 * bstep),
                 (__attribute__((address_space(3))) void*)(wbase + SLAB + i * NT * 16), 16, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the MFMAs
@@ -508,12 +545,15 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     // one MFMA group (a sub-step, 8 MFMAs) with the next group's fragment
     // reads interleaved, one read per MFMA
     auto interleave = [&]() {
+        // LDS reads of a sub-step (a K-major B fragment takes two) and MFMAs
+        constexpr int R = 4 + (KMAJOR ? 2 : 1) * NJ, M = 4 * NJ, P = R < M ? R : M;
 #pragma unroll
-        for (int i = 0; i < 4 + NJ; ++i) {
+        for (int i = 0; i < P; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ - (4 + NJ), 0);
+        if constexpr (M > P) __builtin_amdgcn_sched_group_barrier(0x008, M - P, 0);
+        if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     bf16x8 xa[4], xb[NJ], ya[4], yb[NJ];
@@ -688,14 +728,14 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
 #define SFFN_GEMM256_WN 4        // waves along N in the 256 x 256 tiles (2: 4 waves, 4: 8 waves)
 #endif
 
-template <int EPI>
+template <int EPI, bool KMAJOR = false>
 static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int stage) {
     constexpr int WN = SFFN_GEMM256_WN;
     const int m_tiles = (int)((p.M + TM - 1) / TM);
     constexpr int TNC = (EPI == EPI_GATEUP || EPI == EPI_AMP || EPI == EPI_UV) ? TN / 2 : TN;
     const int n_tiles = (p.N + TNC - 1) / TNC;
-    xlaunch(events, stage, k_gemm256<EPI, WN>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0, s, p,
-            m_tiles, n_tiles);
+    xlaunch(events, stage, k_gemm256<EPI, WN, KMAJOR>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0, s,
+            p, m_tiles, n_tiles);
 }
 
 template <int EPI>
@@ -706,6 +746,20 @@ static void gemm(const GemmParams& p, hipStream_t s, void* const* events, int st
         xlaunch(events, stage, k_gemm<EPI, true>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, p);
     else
         xlaunch(events, stage, k_gemm<EPI, false>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, p);
+}
+
+// Y = bf16(H W_d^T) with W_d^T given K-major ([d_i][d]; K = d_i is a
+// multiple of 64 for every layer): 256-wide tiles for T >= 256, else 128-wide
+static void down_gemm(const uint16_t* h, const uint16_t* WdT, int64_t T, int d, int d_i, uint16_t* y,
+                      hipStream_t s, void* const* events, int stage) {
+    GemmParams g{};
+    g.A = h; g.B0 = WdT; g.M = T; g.N = d; g.K = d_i; g.Cb = y;
+    if (T >= 256) {
+        gemm256<EPI_BF16, true>(g, s, events, stage);
+    } else {
+        const int64_t mt = (T + BM - 1) / BM, nt = (d + BN - 1) / BN;
+        xlaunch(events, stage, k_gemm<EPI_BF16, true, true>, dim3((unsigned)(mt * nt)), dim3(256), 0, s, g);
+    }
 }
 
 // Sum of K-split partials in a fixed order, rounded to bf16.
@@ -751,10 +805,7 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
         g.mask = a.mask; g.gate = a.gate; g.dense = dense_tiles ? 1 : 0;
         if (big) gemm256<EPI_GATEUP>(g, s, a.events, 3);
         else gemm<EPI_GATEUP>(g, s, a.events, 3);
-        g = GemmParams{};
-        g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
-        if (big) gemm256<EPI_BF16>(g, s, a.events, 4);
-        else gemm<EPI_BF16>(g, s, a.events, 4);
+        down_gemm(a.h, a.W_dT, a.T, a.d, a.d_i, a.y, s, a.events, 4);
         return hipGetLastError();
     }
     // Z = bf16(X A^T)
@@ -804,10 +855,7 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     if (big) gemm256<EPI_GATEUP>(g, s, a.events, 3);
     else gemm<EPI_GATEUP>(g, s, a.events, 3);
     // Y = bf16(H W_d^T)
-    g = GemmParams{};
-    g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
-    if (big) gemm256<EPI_BF16>(g, s, a.events, 4);
-    else gemm<EPI_BF16>(g, s, a.events, 4);
+    down_gemm(a.h, a.W_dT, a.T, a.d, a.d_i, a.y, s, a.events, 4);
     return hipGetLastError();
 }
 
@@ -894,10 +942,7 @@ hipError_t launch_amp_mfma(const MfmaArgs& a, hipStream_t s) {
     g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;
     g.mask_w = a.mask; g.keep = a.keep; g.Cf = a.logits_requested ? a.logits : nullptr;
     gemm256<EPI_AMP>(g, s, a.events, 0);
-    g = GemmParams{};
-    g.A = a.h; g.B0 = a.W_d; g.M = a.T; g.N = a.d; g.K = a.d_i; g.Cb = a.y;
-    if (a.T >= 256) gemm256<EPI_BF16>(g, s, a.events, 1);
-    else gemm<EPI_BF16>(g, s, a.events, 1);
+    down_gemm(a.h, a.W_dT, a.T, a.d, a.d_i, a.y, s, a.events, 1);
     skip_stages(a.events, 2, s);
     return hipGetLastError();
 }

@@ -100,7 +100,7 @@ struct MfmaArgs {
     const float* bias;      // [d_i] or null
     const uint16_t* W_g;    // [d_i, d]
     const uint16_t* W_u;    // [d_i, d]
-    const uint16_t* W_d;    // [d, d_i]
+    const uint16_t* W_dT;   // [d_i, d]: W_d transposed, read K-major by the down GEMMs
     uint16_t* y;            // [T, d]
     uint16_t* z;            // [T, rank]   workspace
     float* logits;          // [T, d_i]

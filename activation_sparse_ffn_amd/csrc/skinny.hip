@@ -19,7 +19,7 @@
 // Upcycling", gist.science technical summary, Methodologie > 1. Architectuur
 // and 3. Hardware Implicaties):
 //   Z = bf16(X A^T)  P = Z B^T + bias  mask = top-k(P)
-//   H = select(m, s u v, 0) with U = X W_g^T, V = X W_u^T   Y = bf16(H W_d^T)
+//   H = select(m, s u v, 0) with U = X W_g^T, V = X W_u^T   Y = bf16(H W_d^T) (K-major W_d^T)
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -213,6 +213,135 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
         }
 }
 
+// The down projection Y = H W_d^T with W_d^T K-major ([K = d_i][N = d]): a
+// workgroup owns 64 columns of Y (128-byte pieces of 64 consecutive K-rows
+// per K step: whole cache lines) and a K range; its four waves take
+// interleaved 64-wide K steps, U = 1 fetch ahead in registers. All
+// workgroups walk their K range from its start, so the 64 workgroups of a K
+// range read the 128-byte pieces of the same K-rows at about the same time
+// (starting each at a different step, as k_skinny does for its row-major
+// tiles, cost ~3% here). A step's
+// weight tile (64 K-rows x 128 bytes, fetched eight lanes per row) goes to
+// wave-private LDS with its chunks swizzled for the transposed fragment
+// reads (kmajor_frag); the token tile (H, K-contiguous) as in k_skinny.
+template <int EPI, int MT>
+__global__ __launch_bounds__(256) void k_skinny_down(const SkinnyParams p) {
+    static_assert(EPI == SK_BF16 || EPI == SK_PARTIAL, "plain or K-split output");
+    constexpr int NC = 2;                           // 32-column output tiles per workgroup
+    constexpr int WT = 64 * 128;                    // weight tile bytes
+    constexpr int AT = 32 * 128;                    // token tile bytes
+    constexpr int STAGE = 4 * (WT + MT * AT);
+    constexpr int RED = 4 * NC * MT * 16 * kWave * 4;
+    __shared__ __attribute__((aligned(16))) char smem[STAGE > RED ? STAGE : RED];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * 64;
+    const int kb0 = blockIdx.y * p.k_split;
+    const int steps = p.k_split / 64;
+    char* const wst = smem + wv * (WT + MT * AT);   // this wave's weight tile, then token tiles
+    const int fr = lane >> 3, fc = lane & 7;
+    // weight rows 8 q + fr of a step, chunk fc; token rows mt * 32 + 8 q + fr
+    const uint16_t* wsrc = p.B0 + (size_t)(kb0 + fr) * p.N + n0 + 8 * fc;
+    const uint16_t* asrc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) asrc[mt] = p.A + (size_t)(mt * 32 + fr) * p.K + kb0 + 8 * fc;
+    const size_t wq = (size_t)8 * p.N, aq = (size_t)8 * p.K;
+
+    f32x16 acc[NC][MT];
+#pragma unroll
+    for (int b = 0; b < NC; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[b][mt][v] = 0.f;
+    const int r = lane & 31, h = lane >> 5;
+    struct Fetch { uint4 w[8]; uint4 a[MT][4]; };
+    auto fetch = [&](Fetch& f, int st) {
+        if (st >= steps) return;
+        const int ks = st;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            Raw<uint16_t> rw;
+            rw.load_stream(wsrc + (size_t)64 * ks * p.N + q * wq);   // weights: read once per call
+            f.w[q] = rw.w;
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool valid = mt * 32 + 8 * q + fr < p.M;
+                f.a[mt][q] = valid ? *reinterpret_cast<const uint4*>(asrc[mt] + 64 * ks + q * aq)
+                                   : make_uint4(0, 0, 0, 0);
+            }
+    };
+    auto consume = [&](const Fetch& f, int st) {
+        if (st >= steps) return;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int row = 8 * q + fr;
+            *reinterpret_cast<uint4*>(wst + row * 128 + (kmajor_slot<128>(row, fc) << 4)) = f.w[q];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint4*>(wst + WT + mt * AT + tile_off(8 * q + fr, fc)) = f.a[mt][q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x8 fb[NC], fa[MT];
+#pragma unroll
+            for (int b = 0; b < NC; ++b) fb[b] = kmajor_frag<128>(wst, 32 * b, i, lane);
+            // lane (r, h) of sub-step i carries K = 16 i + 8 h .. + 8, the K that
+            // the transposed weight fragment gives it
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                fa[mt] = *reinterpret_cast<const bf16x8*>(wst + WT + mt * AT + tile_off(r, 2 * i + h));
+#pragma unroll
+            for (int b = 0; b < NC; ++b)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[b], acc[b][mt], 0, 0, 0);
+        }
+    };
+    Fetch f0, f1;
+    fetch(f0, wv);
+    for (int st = wv; st < steps; st += 8) {
+        fetch(f1, st + 4);
+        consume(f0, st);
+        fetch(f0, st + 8);
+        consume(f1, st + 4);
+    }
+
+    // the four waves' partial sums meet in LDS; wave w finishes elements
+    // v = 4 w .. 4 w + 3 of every accumulator tile
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);     // [4][NC * MT * 16][64]
+    auto R = [&](int wave, int e, int ln) -> float& { return red[((size_t)wave * NC * MT * 16 + e) * kWave + ln]; };
+#pragma unroll
+    for (int b = 0; b < NC; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) R(wv, (b * MT + mt) * 16 + v, lane) = acc[b][mt][v];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NC; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int v = 4 * wv + q;
+                const int m = mt * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
+                const int e = (b * MT + mt) * 16 + v;
+                const float val = (R(0, e, lane) + R(1, e, lane)) + (R(2, e, lane) + R(3, e, lane));
+                const int n = n0 + 32 * b + r;
+                if (m >= p.M || n >= p.N) continue;
+                const size_t o = (size_t)m * p.N + n;
+                if constexpr (EPI == SK_PARTIAL) p.partial[(size_t)blockIdx.y * p.M * p.N + o] = val;
+                else p.Cb[o] = f32_to_bf16(val);
+            }
+}
+
 // Sum of the K-split partials in a fixed order, rounded to bf16.
 __global__ __launch_bounds__(256) void k_skinny_sum_bf16(const float* __restrict__ partial,
                                                          uint16_t* __restrict__ C, int splits,
@@ -252,10 +381,40 @@ static int k_splits(int N, int K) {
     return s;
 }
 
+// K splits of the K-major down projection (64 columns per workgroup)
+static int down_splits(int N, int K) {
+    int s = 1;
+    while ((N / 64) * s < 384 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 256) s *= 2;
+    return s;
+}
+
 size_t skinny_partial_floats(int64_t T, int d, int rank, int d_i) {
     const size_t a = (size_t)k_splits(rank, d) * T * rank;
-    const size_t b = (size_t)k_splits(d, d_i) * T * d;
+    const size_t b = (size_t)down_splits(d, d_i) * T * d;
     return a > b ? a : b;
+}
+
+
+// Y = bf16(H W_d^T), W_d^T K-major, as the stage `stage` of the events
+static void skinny_down(const uint16_t* h, const uint16_t* WdT, int M, int d, int d_i, uint16_t* y, float* partial,
+                        hipStream_t s, void* const* ev, int stage) {
+    SkinnyParams p{};
+    p.A = h; p.B0 = WdT; p.M = M; p.N = d; p.K = d_i;
+    const int sp = down_splits(d, d_i);
+    p.k_split = d_i / sp;
+    const dim3 grid((unsigned)(d / 64), (unsigned)sp);
+    hipEvent_t e0 = ev ? static_cast<hipEvent_t>(ev[2 * stage]) : nullptr;
+    hipEvent_t e1 = ev ? static_cast<hipEvent_t>(ev[2 * stage + 1]) : nullptr;
+    if (sp == 1) {
+        p.Cb = y;
+        if (M <= 32) hipExtLaunchKernelGGL(k_skinny_down<SK_BF16, 1>, grid, dim3(256), 0, s, e0, e1, 0u, p);
+        else hipExtLaunchKernelGGL(k_skinny_down<SK_BF16, 2>, grid, dim3(256), 0, s, e0, e1, 0u, p);
+        return;
+    }
+    p.partial = partial;
+    if (M <= 32) hipExtLaunchKernelGGL(k_skinny_down<SK_PARTIAL, 1>, grid, dim3(256), 0, s, e0, nullptr, 0u, p);
+    else hipExtLaunchKernelGGL(k_skinny_down<SK_PARTIAL, 2>, grid, dim3(256), 0, s, e0, nullptr, 0u, p);
+    sum_bf16(partial, y, sp, (int64_t)M * d, s, ev, stage);
 }
 
 hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t s) {
@@ -296,19 +455,7 @@ hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t 
     p.P = a.logits; p.mask = a.mask; p.gate = a.gate;
     skinny<SK_GATEUP, 2>(p, 1, s, a.events, 3, true);
     // Y = bf16(H W_d^T)
-    {
-        const int sp = k_splits(a.d, a.d_i);
-        p = SkinnyParams{};
-        p.A = a.h; p.B0 = a.W_d; p.M = M; p.N = a.d; p.K = a.d_i;
-        if (sp == 1) {
-            p.Cb = a.y;
-            skinny<SK_BF16, 1>(p, 1, s, a.events, 4, true);
-        } else {
-            p.partial = partial;
-            skinny<SK_PARTIAL, 1>(p, sp, s, a.events, 4, false);
-            sum_bf16(partial, a.y, sp, (int64_t)M * a.d, s, a.events, 4);
-        }
-    }
+    skinny_down(a.h, a.W_dT, M, a.d, a.d_i, a.y, partial, s, a.events, 4);
     return hipGetLastError();
 }
 
@@ -322,17 +469,7 @@ hipError_t launch_amp_skinny(const MfmaArgs& a, float* partial, hipStream_t s) {
     hipError_t e = launch_amp_mask(a.logits, a.T, a.d_i, a.keep, a.mask, a.h, s, a.events, 1);
     if (e != hipSuccess) return e;
     // Y = bf16(H W_d^T)
-    const int sp = k_splits(a.d, a.d_i);
-    p = SkinnyParams{};
-    p.A = a.h; p.B0 = a.W_d; p.M = M; p.N = a.d; p.K = a.d_i;
-    if (sp == 1) {
-        p.Cb = a.y;
-        skinny<SK_BF16, 1>(p, 1, s, a.events, 2, true);
-    } else {
-        p.partial = partial;
-        skinny<SK_PARTIAL, 1>(p, sp, s, a.events, 2, false);
-        sum_bf16(partial, a.y, sp, (int64_t)M * a.d, s, a.events, 2);
-    }
+    skinny_down(a.h, a.W_dT, M, a.d, a.d_i, a.y, partial, s, a.events, 2);
     skip_stages(a.events, 3, s);
     return hipGetLastError();
 }

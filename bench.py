@@ -248,6 +248,13 @@ def copy_calibration(args):
           flush=True)
 
 
+def prime(stream):
+    """Enqueue ~0.1 ms of GPU spinning on `stream` (not part of any step)."""
+    import torch
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(250_000)
+
+
 def dev(a):
     """A numpy array (bf16 bit patterns as uint16, or fp32) as a GPU tensor."""
     import numpy as np
@@ -274,6 +281,7 @@ def topk_stress(steps, warmup, ties="random"):
         sffn.bank_topk(p, 16, mask_out=mask)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prime(torch.cuda.current_stream())
     e0.record()
     for _ in range(steps):
         sffn.bank_topk(p, 16, mask_out=mask)
@@ -317,6 +325,7 @@ def backward_bench(ffns, steps, warmup, keep, gate):
         ffns[i % n_layers].backward(x, gy, masks[i % n_layers], workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prime(torch.cuda.current_stream())
     e0.record()
     for i in range(K):
         ffns[i % n_layers].backward(x, gy, masks[i % n_layers], workspace=ws)
@@ -415,6 +424,10 @@ def forward_bench(name, ffns, shape, K, W, keep, gate, graph=True, n_streams=1):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
+        # an untimed spin of ~0.1 ms ahead of the start event keeps the GPU
+        # busy while the host submits the timed steps, so that the events
+        # time the steps' execution and not the host's launch of the first
+        prime(stream)
         e0.record(stream)
         for _ in range(reps):
             g.replay()

@@ -57,8 +57,9 @@ def test_packed_size_and_config_checks(lib):
     size = lib.sparse_ffn_packed_size(ctypes.byref(_cfg()))
     e = 2
     d, di, r = 4096, 14336, 448
-    assert size >= e * (r * d + di * r + 4 * di * d) + 4 * di
-    assert size < e * (r * d + di * r + 4 * di * d) + 4 * di + 8 * 256
+    # A, B, W_g, W_u and W_d^T (one copy of the down projection) and the bias
+    assert size >= e * (r * d + di * r + 3 * di * d) + 4 * di
+    assert size < e * (r * d + di * r + 3 * di * d) + 4 * di + 8 * 256
     for bad in (dict(bank=32), dict(keep=0), dict(keep=65), dict(d_i=1000), dict(d=100),
                 dict(rank=40), dict(d=0), dict(dtype=7), dict(gate=3), dict(d_i=65536 + 64),
                 dict(flags=2), dict(flags=-1)):
