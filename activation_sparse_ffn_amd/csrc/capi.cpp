@@ -115,7 +115,7 @@ struct WsGather {
     size_t z, ids, pk, h, partial, mask, amp, logits, total;
 };
 struct WsMfma {
-    size_t z, logits, mask, h, partial, gate, zpart, total;
+    size_t z, logits, mask, h, partial, gate, zpart, unionw, total;
 };
 
 bool use_skinny(const sffn_config_t& c, int64_t T) {
@@ -158,6 +158,8 @@ WsMfma ws_mfma(const sffn_config_t& c, int64_t T) {
     w.zpart = off;
     const int zs = use_skinny(c, T) ? 1 : sffn::z_splits(T, c.d);
     if (zs > 1) off += align_up((size_t)zs * T * c.rank * 4);
+    w.unionw = off;
+    if (use_skinny(c, T)) off += align_up(nb * 8);
     w.total = off;
     return w;
 }
@@ -382,6 +384,7 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
                            ? at<uint16_t>(workspace, w.gate) : nullptr;
         a.z_partial = (!use_skinny(c, T) && sffn::z_splits(T, c.d) > 1) ? at<float>(workspace, w.zpart)
                                                                          : nullptr;
+        a.union_w = use_skinny(c, T) ? at<uint64_t>(workspace, w.unionw) : nullptr;
         a.need_pred = need_pred;
         a.mask_requested = mask_out != nullptr;
         a.events = h->profiling ? h->events : nullptr;

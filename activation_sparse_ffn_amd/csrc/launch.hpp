@@ -56,9 +56,12 @@ constexpr int kGateTileRows = 256, kGateTileCols = 128;
 constexpr uint16_t kGateDropped = 0xbc00;   // fp16 -1.0
 
 // ---- bank top-k of fp32 logits [T, d_i]: mask words, optional kept ids ------
+// union_out (d_i / 64 words) or null: receives the or of the T tokens' mask
+// words of each bank (T <= 64, no ids)
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s,
-                            void* const* events = nullptr, int stage = 0);
+                            void* const* events = nullptr, int stage = 0,
+                            uint64_t* union_out = nullptr);
 
 // ---- token-gather path (VALU; decode and fp32 layers) ---------------------
 struct GatherArgs {
@@ -107,6 +110,7 @@ struct MfmaArgs {
     uint64_t* mask;         // [T, d_i/64]
     uint16_t* h;            // [T, d_i]    workspace
     uint16_t* gate_tiles;   // fp16 gate tiles (see launch_bank_topk) or null
+    uint64_t* union_w;      // skinny path: [d_i / 64] or of the batch's mask words
     float* z_partial;       // [z_splits, T, rank] K-split partials of z, or null
     bool logits_requested;  // logits points at the caller's logits_out
     bool need_pred;         // false: every channel kept with the silu gate and no

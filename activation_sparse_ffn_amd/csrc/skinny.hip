@@ -40,6 +40,10 @@ struct SkinnyParams {
     const float* P;        // gate/up: logits [M, N]
     const uint64_t* mask;  // gate/up: [M, N / 64]
     int gate;              // 0 predictor, 1 silu
+    // [N / 64 (gate/up) or K / 64 (down)] or null: the or of the batch's mask
+    // words (written by the top-k); weight rows of channels no token keeps
+    // are not read (their products with the token operand are exact zeros)
+    uint64_t* unionw;
 };
 
 // byte offset of 16-byte chunk c of row r in a 32 x 128-byte LDS tile; the
@@ -88,6 +92,16 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
             for (int v = 0; v < 16; ++v) acc[b][mt][v] = 0.f;
 
     const int r = lane & 31, h = lane >> 5;
+    // gate/up: this lane's weight rows 8 q + fr of the tile, kept by some token?
+    uint32_t live = 0xfu;
+    if constexpr (EPI == SK_GATEUP) {
+        if (p.unionw != nullptr) {
+            const uint64_t uw = p.unionw[n0 >> 6] >> (n0 & 63);
+            live = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) live |= (uint32_t)((uw >> (8 * q + fr)) & 1ull) << q;
+        }
+    }
     // Workgroups start their K walk at different steps: rows of one weight
     // matrix sit a power-of-two stride apart, and if every workgroup read the
     // same K offset at the same time the requests would crowd a few HBM
@@ -107,9 +121,13 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
                         const uint16_t* at = src[t] + q * rstride8 + 64 * kstep(s_);
                         if (t < NB) {
                             // weight rows: read once per call, streamed past the caches
-                            Raw<uint16_t> rw;
-                            rw.load_stream(at);
-                            w[u][t][q] = rw.w;
+                            if ((live >> q) & 1u) {
+                                Raw<uint16_t> rw;
+                                rw.load_stream(at);
+                                w[u][t][q] = rw.w;
+                            } else {
+                                w[u][t][q] = make_uint4(0, 0, 0, 0);
+                            }
                         } else {
                             // token rows: re-read by every workgroup from the L2
                             const bool valid = (t - NB) * 32 + 8 * q + fr < p.M;
@@ -255,15 +273,26 @@ __global__ __launch_bounds__(256) void k_skinny_down(const SkinnyParams p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[b][mt][v] = 0.f;
     const int r = lane & 31, h = lane >> 5;
+    // union word of K step (bank) kb0 / 64 + lane, in lane `lane` (the K
+    // range spans at most 64 banks when the union is given)
+    const uint64_t uw_lane = (p.unionw != nullptr && lane < steps) ? p.unionw[kb0 / 64 + lane] : ~0ull;
+    const uint32_t uw_lo = (uint32_t)uw_lane, uw_hi = (uint32_t)(uw_lane >> 32);
     struct Fetch { uint4 w[8]; uint4 a[MT][4]; };
     auto fetch = [&](Fetch& f, int st) {
         if (st >= steps) return;
         const int ks = st;
+        // (readlane returns int: widen through uint32_t, not by sign extension)
+        const uint64_t uw = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(uw_hi, ks) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(uw_lo, ks);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            Raw<uint16_t> rw;
-            rw.load_stream(wsrc + (size_t)64 * ks * p.N + q * wq);   // weights: read once per call
-            f.w[q] = rw.w;
+            if ((uw >> (8 * q + fr)) & 1ull) {
+                Raw<uint16_t> rw;
+                rw.load_stream(wsrc + (size_t)64 * ks * p.N + q * wq);   // weights: read once per call
+                f.w[q] = rw.w;
+            } else {
+                f.w[q] = make_uint4(0, 0, 0, 0);                        // no token keeps this channel
+            }
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -397,11 +426,12 @@ size_t skinny_partial_floats(int64_t T, int d, int rank, int d_i) {
 
 // Y = bf16(H W_d^T), W_d^T K-major, as the stage `stage` of the events
 static void skinny_down(const uint16_t* h, const uint16_t* WdT, int M, int d, int d_i, uint16_t* y, float* partial,
-                        hipStream_t s, void* const* ev, int stage) {
+                        const uint64_t* unionw, hipStream_t s, void* const* ev, int stage) {
     SkinnyParams p{};
     p.A = h; p.B0 = WdT; p.M = M; p.N = d; p.K = d_i;
     const int sp = down_splits(d, d_i);
     p.k_split = d_i / sp;
+    if (p.k_split / 64 <= kWave) p.unionw = const_cast<uint64_t*>(unionw);   // a lane per K step
     const dim3 grid((unsigned)(d / 64), (unsigned)sp);
     hipEvent_t e0 = ev ? static_cast<hipEvent_t>(ev[2 * stage]) : nullptr;
     hipEvent_t e1 = ev ? static_cast<hipEvent_t>(ev[2 * stage + 1]) : nullptr;
@@ -420,6 +450,9 @@ static void skinny_down(const uint16_t* h, const uint16_t* WdT, int M, int d, in
 hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t s) {
     const int M = (int)a.T;
     SkinnyParams p{};
+    // the batch's union of kept channels per bank (every channel when the
+    // dense fallback runs no top-k)
+    uint64_t* const unionw = a.need_pred ? a.union_w : nullptr;
     if (!a.need_pred) {
         // every channel kept with the silu gate and no logits asked for: no
         // predictor and no top-k; the gate/up epilogue reads an all-ones mask
@@ -446,16 +479,16 @@ hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t 
         p.A = a.z; p.B0 = a.B; p.M = M; p.N = a.d_i; p.K = a.rank; p.Cf = a.logits; p.bias = a.bias;
         skinny<SK_F32_BIAS, 1>(p, 1, s, a.events, 1, true);
         // mask
-        const hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2);
+        const hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2, unionw);
         if (e != hipSuccess) return e;
     }
     // H = select(m, s u v, 0)
     p = SkinnyParams{};
     p.A = a.x; p.B0 = a.W_g; p.B1 = a.W_u; p.M = M; p.N = a.d_i; p.K = a.d; p.Cb = a.h;
-    p.P = a.logits; p.mask = a.mask; p.gate = a.gate;
+    p.P = a.logits; p.mask = a.mask; p.gate = a.gate; p.unionw = unionw;
     skinny<SK_GATEUP, 2>(p, 1, s, a.events, 3, true);
     // Y = bf16(H W_d^T)
-    skinny_down(a.h, a.W_dT, M, a.d, a.d_i, a.y, partial, s, a.events, 4);
+    skinny_down(a.h, a.W_dT, M, a.d, a.d_i, a.y, partial, unionw, s, a.events, 4);
     return hipGetLastError();
 }
 
@@ -469,7 +502,7 @@ hipError_t launch_amp_skinny(const MfmaArgs& a, float* partial, hipStream_t s) {
     hipError_t e = launch_amp_mask(a.logits, a.T, a.d_i, a.keep, a.mask, a.h, s, a.events, 1);
     if (e != hipSuccess) return e;
     // Y = bf16(H W_d^T)
-    skinny_down(a.h, a.W_dT, M, a.d, a.d_i, a.y, partial, s, a.events, 2);
+    skinny_down(a.h, a.W_dT, M, a.d, a.d_i, a.y, partial, nullptr, s, a.events, 2);
     skip_stages(a.events, 3, s);
     return hipGetLastError();
 }
