@@ -154,7 +154,8 @@ WsMfma ws_mfma(const sffn_config_t& c, int64_t T) {
     w.partial = off;
     if (use_skinny(c, T)) off += align_up(sffn::skinny_partial_floats(T, c.d, c.rank, c.d_i) * 4);
     w.gate = off;
-    if (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0) off += align_up(sffn::gate_tiles_bytes(T, c.d_i));
+    if (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0)
+        off += align_up(sffn::gate_tiles_bytes(T, c.d_i, c.keep, as_int(c.gate)));
     w.zpart = off;
     const int zs = use_skinny(c, T) ? 1 : sffn::z_splits(T, c.d);
     if (zs > 1) off += align_up((size_t)zs * T * c.rank * 4);
@@ -381,7 +382,7 @@ sffn_status_t sparse_ffn_forward(sffn_handle_t h, const void* x, int64_t T, void
         a.mask = mask_out ? mask_out : at<uint64_t>(workspace, w.mask);
         a.h = at<uint16_t>(workspace, w.h);
         a.gate_tiles = (!use_skinny(c, T) && c.d_i % sffn::kGateTileCols == 0)
-                           ? at<uint16_t>(workspace, w.gate) : nullptr;
+                           ? at<uint8_t>(workspace, w.gate) : nullptr;
         a.z_partial = (!use_skinny(c, T) && sffn::z_splits(T, c.d) > 1) ? at<float>(workspace, w.zpart)
                                                                          : nullptr;
         a.union_w = use_skinny(c, T) ? at<uint64_t>(workspace, w.unionw) : nullptr;

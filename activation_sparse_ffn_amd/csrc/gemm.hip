@@ -39,14 +39,14 @@ struct GemmParams {
     const float* bias;   // [N] or null
     const float* P;      // gate/up: logits [M, N]
     const uint64_t* mask;// gate/up: [M, N/64]
-    const uint16_t* G;   // gate/up, 256-row tiles: fp16 gate tiles instead of P and mask
+    const uint8_t* G;    // gate/up, 256-row tiles: gate tiles instead of P and mask
     int gate;            // 0 predictor, 1 silu
     int kn;              // EPI_PARTIAL: K range of one split (blockIdx.y selects the split)
     // EPI_TOPK: logits (+ bias) go through LDS into the bank top-k; Cf receives
     // the logits only when non-null
     uint64_t* mask_w;    // [M, N/64]
-    uint16_t* gate_w;    // fp16 gate tiles
-    int keep;
+    uint8_t* gate_w;     // gate tiles (layout: gate_row_bytes)
+    int keep;            // EPI_TOPK, and the gate tiles' layout
     int dense;           // EPI_GATEUP without gate tiles: every channel kept (silu gate)
     uint16_t* Cb2;       // EPI_UV: bf16 [M, N] receives V (Cb receives U)
 };
@@ -322,9 +322,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
             for (int c = 0; c < 16; ++c) reinterpret_cast<float4*>(p.Cf + t * p.N + j0)[c] = ld(c);
         }
         const int col_tiles = p.N / kGateTileCols;
-        uint16_t* gp = p.gate_w + ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) *
-                                      (kGateTileRows * kGateTileCols) +
-                       (t % kGateTileRows) * kGateTileCols + j0 % kGateTileCols;
+        const int rb = gate_row_bytes(p.keep, p.gate);
+        uint8_t* const grow = p.gate_w +
+                              ((size_t)(t / kGateTileRows) * col_tiles + j0 / kGateTileCols) * (kGateTileRows * rb) +
+                              (size_t)(t % kGateTileRows) * rb;
+        if (gate_compact(p.keep)) {
+            // compact row: this bank's kept channel positions in channel
+            // order and (predictor gate) their sigmoid(p), built in registers
+            const int ib = gate_ids_bytes(p.keep), vb = gate_vals_bytes(p.keep);
+            const bool pred = p.gate == kGatePredictor;
+            constexpr int IW = (kGateCompactMax + 15) / 16 * 4, VW = (2 * kGateCompactMax + 15) / 16 * 4;
+            uint32_t idw[IW], vw[VW];
+#pragma unroll
+            for (int w = 0; w < IW; ++w) idw[w] = 0;
+#pragma unroll
+            for (int w = 0; w < VW; ++w) vw[w] = 0;
+            uint64_t m = sel;
+            // fully unrolled (register indices fixed at compile time), each
+            // step under a uniform test instead of a loop exit
+#pragma unroll
+            for (int k = 0; k < kGateCompactMax; ++k) {
+                if (k < p.keep) {
+                    const int c = __builtin_ctzll(m);
+                    m &= m - 1;
+                    idw[k >> 2] |= (uint32_t)c << (8 * (k & 3));
+                    if (pred) {
+                        const float v = *reinterpret_cast<const float*>(trow + 4 * c);
+                        vw[k >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sigmoidf_dev(v))
+                                      << (16 * (k & 1));
+                    }
+                }
+            }
+            uint8_t* const gi = grow + bsel * ib;
+#pragma unroll
+            for (int c = 0; c < IW / 4; ++c)
+                if (16 * c < ib)
+                    *reinterpret_cast<uint4*>(gi + 16 * c) =
+                        make_uint4(idw[4 * c], idw[4 * c + 1], idw[4 * c + 2], idw[4 * c + 3]);
+            if (pred) {
+                uint8_t* const gv = grow + 2 * ib + bsel * vb;
+#pragma unroll
+                for (int c = 0; c < VW / 4; ++c)
+                    if (16 * c < vb)
+                        *reinterpret_cast<uint4*>(gv + 16 * c) =
+                            make_uint4(vw[4 * c], vw[4 * c + 1], vw[4 * c + 2], vw[4 * c + 3]);
+            }
+            return;
+        }
+        uint16_t* const gp = reinterpret_cast<uint16_t*>(grow) + j0 % kGateTileCols;
         // gate values: sigmoid(p) (predictor gate) or 1 (silu gate) where kept
         auto pack = [&](auto gate_of) {
 #pragma unroll
@@ -475,12 +520,12 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         }
     };
     const size_t bstep = KMAJOR ? (size_t)p.N : 1;     // B elements per unit of K
-    // gate/up with gate tiles: the 256 x 128 fp16 gate tile of an output block
-    // is one contiguous 64 KB block
-    auto gate_tile = [&](int mtile, int ntile) -> const uint16_t* {
+    // gate/up with gate tiles: the gate tile of a 256 x 128 output block is
+    // one contiguous block of 256 rows (at most 64 KB)
+    auto gate_tile = [&](int mtile, int ntile) -> const uint8_t* {
         if constexpr (EPI == EPI_GATEUP)
             if (p.G != nullptr)
-                return p.G + ((size_t)mtile * (p.N / kGateTileCols) + ntile) * (TM * kGateTileCols);
+                return p.G + ((size_t)mtile * (p.N / kGateTileCols) + ntile) * (TM * gate_row_bytes(p.keep, p.gate));
         return nullptr;
     };
 
@@ -528,13 +573,17 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         }
         __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the MFMAs
     };
-    // the gate tile as a plain copy (row pitch 256 bytes)
-    auto fetch_gate = [&](const uint16_t* gt, char* dst) {
+    // the gate tile as a plain copy of its 16-byte chunks. The loop always
+    // issues the full tile's count of loads (no branch in the K loop); past
+    // a compact tile's end they repeat its last chunk into LDS bytes that
+    // nothing reads.
+    auto fetch_gate = [&](const uint8_t* gt, char* dst) {
+        const int last = TM * gate_row_bytes(p.keep, p.gate) / 16 - 1;
         char* wbase = dst + wv * (kWave * 16);
 #pragma unroll
         for (int i = 0; i < TM * kGateTileCols * 2 / (NT * 16); ++i)
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(gt + (size_t)(tid + i * NT) * 8),
+                (const __attribute__((address_space(1))) void*)(gt + (size_t)min(tid + i * NT, last) * 16),
                 (__attribute__((address_space(3))) void*)(wbase + i * NT * 16), 16, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -557,7 +606,46 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         __builtin_amdgcn_sched_barrier(0);
     };
     bf16x8 xa[4], xb[NJ], ya[4], yb[NJ];
-    const uint16_t* gtile = nullptr;          // gate tile of the current output block, if any
+    const uint8_t* gtile = nullptr;           // gate tile of the current output block, if any
+    bool compact = false;                     // gtile in the compact layout
+    // A compact gate tile (at src) expanded into the full fp16 layout (at
+    // dst), one (row, bank) per thread: -1 everywhere, then each kept
+    // channel's value at its position.
+    auto expand = [&](const char* src, char* dst) {
+        const int ib = gate_ids_bytes(p.keep), vb = gate_vals_bytes(p.keep);
+        const int rb = gate_row_bytes(p.keep, p.gate);
+        const uint32_t dropped2 = (uint32_t)kGateDropped * 0x10001u;
+        const bool pred = p.gate == kGatePredictor;
+        for (int q = tid; q < 2 * TM; q += NT) {
+            const int row = q >> 1, bsel = q & 1;
+            const char* gi = src + row * rb + bsel * ib;
+            const char* gv = src + row * rb + 2 * ib + bsel * vb;
+            char* const er = dst + row * 256 + bsel * 128;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)     // rotated by lane: neighbours start on different banks
+                *reinterpret_cast<uint4*>(er + 16 * ((c + lane) & 7)) =
+                    make_uint4(dropped2, dropped2, dropped2, dropped2);
+            // 16 kept channels at a time: their positions (one 16-byte
+            // chunk) and values (two), requested together
+            for (int k0 = 0; k0 < p.keep; k0 += 16) {
+                const uint4 ids = *reinterpret_cast<const uint4*>(gi + k0);
+                const uint32_t iw[4] = {ids.x, ids.y, ids.z, ids.w};
+                uint32_t vw[8];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    uint4 w = make_uint4(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);   // fp16 1: silu
+                    if (pred && 2 * k0 + 16 * c < vb) w = *reinterpret_cast<const uint4*>(gv + 2 * k0 + 16 * c);
+                    vw[4 * c] = w.x; vw[4 * c + 1] = w.y; vw[4 * c + 2] = w.z; vw[4 * c + 3] = w.w;
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int c = (iw[k >> 2] >> (8 * (k & 3))) & 63;
+                    if (k0 + k < p.keep)
+                        *reinterpret_cast<uint16_t*>(er + 2 * c) = (uint16_t)(vw[k >> 1] >> (16 * (k & 1)));
+                }
+            }
+        }
+    };
     // K step kt from slab `cur` (sub-step 0 already in x); the barrier sits
     // before the last sub-step, so that sub-step's MFMAs cover the barrier
     // and the first reads of the next slab
@@ -575,6 +663,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
 
     sources(m0, n0);
     gtile = gate_tile(mt, nt);
+    compact = gtile != nullptr && gate_compact(p.keep);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -655,6 +744,16 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         return;
     }
     if constexpr (EPI == EPI_GATEUP) {
+        if (compact) {
+            // the compact gate tile, expanded into the full layout in the
+            // other slab buffer. With two or more K steps the tile landed
+            // before the last step's barrier, after which no wave reads that
+            // buffer; a single step fetched it after its barrier.
+            if (kt_n == 1) landed();
+            char* const ebuf = gbuf == buf0 ? buf1 : buf0;
+            expand(gbuf, ebuf);
+            gbuf = ebuf;
+        }
         if (gtile != nullptr || p.dense) {
             // H = select(kept, s u v, 0) with the gate values of the LDS
             // copy of the gate tile, written over them in place (each
@@ -851,7 +950,7 @@ hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s) {
     // H = select(m, s u v, 0)
     g = GemmParams{};
     g.A = a.x; g.B0 = a.W_g; g.B1 = a.W_u; g.M = a.T; g.N = a.d_i; g.K = a.d; g.Cb = a.h;
-    g.P = a.logits; g.mask = a.mask; g.gate = a.gate; g.G = tiles ? a.gate_tiles : nullptr;
+    g.P = a.logits; g.mask = a.mask; g.gate = a.gate; g.keep = a.keep; g.G = tiles ? a.gate_tiles : nullptr;
     if (big) gemm256<EPI_GATEUP>(g, s, a.events, 3);
     else gemm<EPI_GATEUP>(g, s, a.events, 3);
     // Y = bf16(H W_d^T)

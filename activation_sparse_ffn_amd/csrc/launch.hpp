@@ -48,12 +48,32 @@ inline void xlaunch(void* const* events, int stage, F kernel, dim3 grid, dim3 bl
 
 // ---- gate tiles ------------------------------------------------------------
 // Gate input of the 256 x 128 gate/up GEMM tiles (d_i % 128 == 0), written by
-// the fused predictor-layer-2 + top-k GEMM: fp16 bits, tile-contiguous,
-// G[t / 256][j / 128][t % 256][j % 128] = sigmoid(p) (predictor gate) or 1
-// (silu gate) for kept channels, -1 for dropped ones. Rows t >= T of the last
-// tile are not written.
+// the fused predictor-layer-2 + top-k GEMM, one contiguous tile per output
+// block (t / 256, j / 128) of 256 rows (tokens) of gate_row_bytes each. Rows
+// t >= T of the last tile are not written.
+//  * compact (keep <= kGateCompactMax): a row holds, for each of the block's
+//    two banks, the kept channels' positions in the bank (one byte each, in
+//    channel order, padded to gate_ids_bytes), then, for the predictor gate
+//    only, for each bank their fp16 sigmoid(p) in the same order (padded to
+//    gate_vals_bytes).
+//  * full (keep > kGateCompactMax): fp16 G[t % 256][j % 128] = sigmoid(p)
+//    (predictor gate) or 1 (silu gate) for kept channels, -1 for dropped ones.
 constexpr int kGateTileRows = 256, kGateTileCols = 128;
 constexpr uint16_t kGateDropped = 0xbc00;   // fp16 -1.0
+constexpr int kGateCompactMax = 40;         // largest keep whose compact row fits 256 bytes
+__host__ __device__ inline bool gate_compact(int keep) { return keep <= kGateCompactMax; }
+__host__ __device__ inline int gate_ids_bytes(int keep) { return (keep + 15) / 16 * 16; }
+__host__ __device__ inline int gate_vals_bytes(int keep) { return (2 * keep + 15) / 16 * 16; }
+__host__ __device__ inline int gate_row_bytes(int keep, int gate) {
+    return gate_compact(keep)
+               ? 2 * gate_ids_bytes(keep) + (gate == kGatePredictor ? 2 * gate_vals_bytes(keep) : 0)
+               : 2 * kGateTileCols;
+}
+// bytes of the gate tiles for T tokens
+inline size_t gate_tiles_bytes(int64_t T, int d_i, int keep, int gate) {
+    return (size_t)((T + kGateTileRows - 1) / kGateTileRows) * (size_t)(d_i / kGateTileCols) * kGateTileRows *
+           (size_t)gate_row_bytes(keep, gate);
+}
 
 // ---- bank top-k of fp32 logits [T, d_i]: mask words, optional kept ids ------
 // union_out (d_i / 64 words) or null: receives the or of the T tokens' mask
@@ -109,7 +129,7 @@ struct MfmaArgs {
     float* logits;          // [T, d_i]
     uint64_t* mask;         // [T, d_i/64]
     uint16_t* h;            // [T, d_i]    workspace
-    uint16_t* gate_tiles;   // fp16 gate tiles (see launch_bank_topk) or null
+    uint8_t* gate_tiles;    // gate tiles (see gate_row_bytes) or null
     uint64_t* union_w;      // skinny path: [d_i / 64] or of the batch's mask words
     float* z_partial;       // [z_splits, T, rank] K-split partials of z, or null
     bool logits_requested;  // logits points at the caller's logits_out
@@ -122,8 +142,6 @@ struct MfmaArgs {
 int z_splits(int64_t T, int d);
 // predictor layer 2 and the bank top-k run as one kernel (with gate tiles)
 bool mfma_fused_topk(int64_t T, int d, int d_i, int rank);
-// bytes of the gate tiles for T tokens
-size_t gate_tiles_bytes(int64_t T, int d_i);
 hipError_t launch_mfma_forward(const MfmaArgs& a, hipStream_t s);
 // the Dense-4x baseline on the MFMA path: dense gate/up with the amplitude
 // top-k in its epilogue (mask, masked bf16 h, amplitudes into logits when

@@ -190,10 +190,6 @@ hipError_t launch_fill_mask(uint64_t* mask, int64_t n_words, hipStream_t s) {
     return hipGetLastError();
 }
 
-size_t gate_tiles_bytes(int64_t T, int d_i) {
-    return (size_t)((T + kGateTileRows - 1) / kGateTileRows) * kGateTileRows * d_i * 2;
-}
-
 // Compute units of the current device, asked once per device (every thread
 // that races on the first call stores the same value).
 static int compute_units() {

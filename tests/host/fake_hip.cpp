@@ -54,7 +54,6 @@ bool fused_ok(const GatherArgs& a) { return a.dt == Dt::BF16 && a.d == 4096 && a
 hipError_t launch_gather_forward(const GatherArgs&, hipStream_t) { return launched(); }
 int z_splits(int64_t T, int d) { return (T >= 256 && d % 256 == 0) ? 4 : 1; }
 bool mfma_fused_topk(int64_t T, int, int d_i, int) { return T >= 256 && d_i % 128 == 0; }
-size_t gate_tiles_bytes(int64_t T, int d_i) { return (size_t)((T + 255) / 256) * 256 * d_i * 2; }
 hipError_t launch_mfma_forward(const MfmaArgs&, hipStream_t) { return launched(); }
 hipError_t launch_amp_mfma(const MfmaArgs&, hipStream_t) { return launched(); }
 hipError_t launch_amp_skinny(const MfmaArgs&, float*, hipStream_t) { return launched(); }

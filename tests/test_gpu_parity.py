@@ -412,6 +412,22 @@ def test_forward_other_keep(mid_layer, keep, T, gate):
     check_forward(mid_layer, x, y, mask, logits, bias=True, keep=keep, gate=gate)
 
 
+@pytest.mark.parametrize("keep", [7, 40, 41])
+@pytest.mark.parametrize("gate", ["pred", "silu"])
+def test_forward_gate_tile_formats(mid_layer, keep, gate):
+    """The gate tiles that the fused predictor-2 + top-k GEMM hands to the
+    256-wide gate/up GEMM (T >= 256) in both layouts: compact rows of kept
+    channel positions and gate values (keep <= 40; 7 leaves padding after
+    both, 40 is the largest compact row and takes three groups of 16) and
+    the full fp16 tile (41). T = 300 leaves the second 256-row tile partly
+    filled."""
+    ffn = make_ffn(mid_layer, bias=True, keep=keep, gate=gate)
+    x = wl.make_tokens(MID, 300, seed=90 + keep)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(mid_layer, x, y, mask, logits, bias=True, keep=keep, gate=gate)
+
+
 @pytest.mark.parametrize("T", [2, 16])
 @pytest.mark.parametrize("gate", ["pred", "silu"])
 def test_keep_all_channels_is_dense(mid_layer, T, gate):
