@@ -10,7 +10,8 @@
 // XOR-swizzled by row pairs) into the v_mfma_f32_32x32x16_bf16 fragment layout:
 // lane (r, h) of sub-step i takes row r, k = 32 h + 8 i .. + 8, for A and B
 // alike (the MFMA only needs both operands to agree on which k each lane
-// carries). Loads run U steps ahead of the matrix cores. The four waves meet
+// carries). The predictor GEMMs' loads run U steps ahead of the matrix cores
+// (gate/up: one fetch per wave at a time). The four waves meet
 // in LDS, where each wave finishes a quarter of the accumulator elements and
 // runs the epilogue (or writes an fp32 partial when K is also split across
 // workgroups).
@@ -52,9 +53,6 @@ __device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + ((c ^ (
 
 #ifndef SFFN_SKINNY_U
 #define SFFN_SKINNY_U 1          // K steps per fetch
-#endif
-#ifndef SFFN_SKINNY_DB
-#define SFFN_SKINNY_DB 1         // 1: two fetches in flight (register double buffer)
 #endif
 
 template <int EPI, int NB, int MT>
@@ -164,25 +162,30 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
             }
         }
     };
-    // two register buffers: the next U steps are in flight while the current
-    // U steps go through LDS into the matrix cores
+    // One weight tile per step (predictor GEMMs): two register buffers, so
+    // the next U steps are in flight while the current U steps go through
+    // LDS into the matrix cores. Two weight tiles per step (gate/up): one
+    // buffer; the other waves of the compute unit keep the memory system
+    // busy, and with two fetches in flight per wave (~44 MB requested across
+    // the chip) the requests congest it: the 32-token gate/up took 41.3 us
+    // double-buffered and 38.5 us single-buffered.
     constexpr int SPAN = 4 * U;                  // step distance covered by one fetch
-#if SFFN_SKINNY_DB
-    uint4 w0[U][NT][4], w1[U][NT][4];
-    fetch(w0, wv);
-    for (int st = wv; st < steps; st += 2 * SPAN) {
-        fetch(w1, st + SPAN);
-        consume(w0, st);
-        fetch(w0, st + 2 * SPAN);
-        consume(w1, st + SPAN);
+    if constexpr (NB == 1) {
+        uint4 w0[U][NT][4], w1[U][NT][4];
+        fetch(w0, wv);
+        for (int st = wv; st < steps; st += 2 * SPAN) {
+            fetch(w1, st + SPAN);
+            consume(w0, st);
+            fetch(w0, st + 2 * SPAN);
+            consume(w1, st + SPAN);
+        }
+    } else {
+        for (int st = wv; st < steps; st += SPAN) {
+            uint4 w0[U][NT][4];
+            fetch(w0, st);
+            consume(w0, st);
+        }
     }
-#else
-    for (int st = wv; st < steps; st += SPAN) {
-        uint4 w0[U][NT][4];
-        fetch(w0, st);
-        consume(w0, st);
-    }
-#endif
 
     // the four waves' partial sums meet in LDS; wave w finishes elements
     // v = 4 w .. 4 w + 3 of every accumulator tile
