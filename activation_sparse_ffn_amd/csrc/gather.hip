@@ -286,12 +286,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
 }
 
 // y = sum of the partial rows in a fixed order: workgroup = (token, 32
-// columns); thread (column, eighth) sums every eighth partial row with all of
-// its loads in flight, then LDS joins the eighths in order.
+// columns) of 32 kReduceParts threads; thread (column, part) sums every
+// kReduceParts-th partial row with all of its loads in flight, then LDS joins
+// the parts in order. 16 parts (512 threads, 14 loads each for the 224 rows
+// of the method's layer) step 0.5 us faster than 8 parts (256 threads, 28
+// loads each).
+constexpr int kReduceParts = 16;
 template <typename E>
-__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ partial, E* __restrict__ y,
-                                                int d, int groups, int col_blocks) {
-    constexpr int Q = 8, PER = 32;                 // eighths, loads per thread per pass
+__global__ __launch_bounds__(32 * kReduceParts) void k_reduce(const float* __restrict__ partial, E* __restrict__ y,
+                                                              int d, int groups, int col_blocks) {
+    constexpr int Q = kReduceParts, PER = 16;        // parts, loads per thread per pass
     __shared__ float red[Q][32];
     const int tid = threadIdx.x, cl = tid & 31, q = tid >> 5;
     const unsigned t = blockIdx.x / (unsigned)col_blocks;
@@ -567,7 +571,7 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
             xlaunch(a.events, 2, k_down<E, false>, dgrid, dim3(256), 0, s, static_cast<const E*>(a.W_dT),
                     a.ids, a.h, a.partial, a.d, d_s, groups, slices);
         const int col_blocks = (a.d + 31) / 32;
-        xlaunch(a.events, 3, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s, a.partial,
+        xlaunch(a.events, 3, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(32 * kReduceParts), 0, s, a.partial,
                 static_cast<E*>(a.y), a.d, groups, col_blocks);
         skip_stages(a.events, 4, s);
         return hipGetLastError();
@@ -596,7 +600,7 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
                         static_cast<const E*>(a.W_u), static_cast<const E*>(a.W_dT), a.rank, a.d_i,
                         a.gate, a.mask, a.logits, a.partial);
                 const int col_blocks = (a.d + 31) / 32;
-                xlaunch(a.events, 2, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
+                xlaunch(a.events, 2, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(32 * kReduceParts), 0, s,
                         a.partial, static_cast<E*>(a.y), a.d, nb, col_blocks);
                 skip_stages(a.events, 3, s);
                 return hipGetLastError();
@@ -631,7 +635,7 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
     }
     {
         const int col_blocks = (a.d + 31) / 32;
-        xlaunch(a.events, 4, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(256), 0, s,
+        xlaunch(a.events, 4, k_reduce<E>, dim3((unsigned)(T * col_blocks)), dim3(32 * kReduceParts), 0, s,
                 a.partial, static_cast<E*>(a.y), a.d, groups, col_blocks);
     }
     return hipGetLastError();
