@@ -325,35 +325,44 @@ __global__ __launch_bounds__(32 * kReduceParts) void k_reduce(const float* __res
 
 // ---------------------------------------------------------------------------
 // Fused decode kernel for the method's layer width (d = 4096): one workgroup
-// of 8 waves per (token, bank) runs predictor layer 2 on the bank's 64 rows of
-// B, the bank top-k, gate/up on the 16 kept rows and the bank's share of the
-// down projection over all d columns, written as one partial row of y.
+// of KEEP waves per (token, bank) runs predictor layer 2 on the bank's 64 rows
+// of B, the bank top-k, gate/up on the KEEP kept rows and the bank's share of
+// the down projection over all d columns, written as one partial row of y.
 // Every wave runs the bank top-k itself (the mask is wave-uniform, so the
 // kept channels come out of it in scalar registers). Wave w computes u and v
-// of kept channels w and w + 8; the weight rows then stream through a bounded
-// window: per thread, the 1 KB chunks of its wave's four gate/up rows and
-// then its 16-byte pieces of the 16 kept W_d^T rows form one ordered stream
+// of kept channel w; the weight rows then stream through a bounded window:
+// per thread, its 1 KB chunks of the wave's W_g and W_u rows and then its
+// 16-byte pieces of its half of the kept W_d^T rows form one ordered stream
 // of 16-byte loads, of which at most kFusedAhead groups of four are in
-// flight. Requesting all of a workgroup's ~400 KB at once (every thread 48
-// loads) congests the memory system; the window streams the same bytes ~3%
-// faster, and the W_d^T rows are still in flight while gate/up finishes.
+// flight (requesting a workgroup's ~400 KB at once congests the memory
+// system). The two halves of the workgroup each sum half of the kept W_d^T
+// rows over all d columns and meet in LDS. 16 waves per bank stream the
+// weight rows ~2% faster than 8 waves with two kept channels each.
 // ---------------------------------------------------------------------------
 constexpr int kFusedD = 4096;
-constexpr int kFusedAhead = 4;   // groups of four 16-byte loads in flight per thread
+constexpr int kFusedAhead = 2;   // groups of four 16-byte loads in flight per thread
 
 template <int KEEP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(64 * KEEP)
 void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
                   const uint16_t* __restrict__ B, const float* __restrict__ bias,
                   const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
                   const uint16_t* __restrict__ WdT, int rank, int d_i, int gate,
                   uint64_t* __restrict__ mask, float* __restrict__ logits,
                   float* __restrict__ partial) {
-    constexpr int D = kFusedD, NW = 8, CPW = KEEP / NW, NCX = D / 8 / kWave;
-    static_assert(KEEP % NW == 0, "kept channels split evenly over the waves");
+    constexpr int D = kFusedD, NW = KEEP, NT = kWave * NW;
+    constexpr int NCX = D / 8 / kWave;            // 16-byte chunks per lane of a gate/up row
+    constexpr int RPW = kBank / NW;               // rows of B per wave
+    constexpr int CPT = D / 8;                    // threads over the d columns (8 each)
+    constexpr int HALVES = NT / CPT;              // thread groups splitting the kept W_d^T rows
+    constexpr int DPH = KEEP / HALVES;            // kept W_d^T rows per thread
+    constexpr int NS = NCX / 2 + DPH / 4;         // steps of the load stream
+    static_assert(NT % CPT == 0 && HALVES == 2 && DPH % 4 == 0 && NCX % 2 == 0 && RPW >= 1,
+                  "the layout of the method's layer: 16 kept of 64, d = 4096");
     __shared__ uint4 xs[D / 8];
     __shared__ float sp[kBank];
     __shared__ float sh[KEEP];
+    __shared__ float4 comb[CPT][2];               // the upper half's sums
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nb = d_i / kBank;
@@ -361,32 +370,32 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     const unsigned b = blockIdx.x - t * (unsigned)nb;
     const int nch = rank / 8;
 
-    // predictor layer 2: wave wv takes rows 64 b + 8 wv .. + 8
-    const size_t row0 = (size_t)b * kBank + 8 * wv;
-    float acc[8];
+    // predictor layer 2: wave wv takes rows 64 b + RPW wv .. + RPW
+    const size_t row0 = (size_t)b * kBank + RPW * wv;
+    float acc[RPW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int i = 0; i < RPW; ++i) acc[i] = 0.f;
     for (int c = lane; c < nch; c += kWave) {
-        Raw<uint16_t> rb[8];
+        Raw<uint16_t> rb[RPW];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rb[i].load(B + (row0 + i) * rank + 8 * c);
+        for (int i = 0; i < RPW; ++i) rb[i].load(B + (row0 + i) * rank + 8 * c);
         const float* zt = z + (size_t)t * rank + 8 * c;
         const float4 z0 = *reinterpret_cast<const float4*>(zt);
         const float4 z1 = *reinterpret_cast<const float4*>(zt + 4);
         const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RPW; ++i) {
             float bv[8];
             rb[i].decode(bv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[i] = fmaf(zv[e], bv[e], acc[i]);
         }
     }
-    xs[tid] = *reinterpret_cast<const uint4*>(x + (size_t)t * D + 8 * tid);
-    reduce_rows<8>(acc, lane);
-    if ((lane & 7) == 0) {
-        const int r = lane >> 3;
-        sp[8 * wv + r] = acc[0] + (bias ? bias[row0 + r] : 0.f);
+    if (tid < CPT) xs[tid] = *reinterpret_cast<const uint4*>(x + (size_t)t * D + 8 * tid);
+    reduce_rows<RPW>(acc, lane);
+    if ((lane & (kWave / RPW - 1)) == 0) {
+        const int r = lane / (kWave / RPW);
+        sp[RPW * wv + r] = acc[0] + (bias ? bias[row0 + r] : 0.f);
     }
     __syncthreads();
 
@@ -403,95 +412,100 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
         for (int i = 0; i < n; ++i) m &= m - 1;
         return m;
     };
-    static_assert(CPW == 2, "two kept channels per wave");
-    // this wave's kept channels (slots wv and wv + NW) and their rows
-    const uint64_t m0 = drop(sel, wv);
-    const uint64_t m1 = drop(m0, NW);
-    const int c0 = __builtin_ctzll(m0), c1 = __builtin_ctzll(m1);
-    const uint16_t* rows[4];
+    // this wave's kept channel (slot wv) and its rows
+    const int c0 = __builtin_ctzll(drop(sel, wv));
+    const size_t j0 = (size_t)b * kBank + c0;
+    const uint16_t* rows[2] = {Wg + j0 * D, Wu + j0 * D};
+    // this thread's kept rows of W_d^T: slots DPH hf .. + DPH - 1, columns
+    // 8 (tid % CPT) .. + 7
+    const int hf = tid / CPT, col = 8 * (tid % CPT);
+    const uint16_t* drow[DPH];
     {
-        const size_t j0 = (size_t)b * kBank + c0, j1 = (size_t)b * kBank + c1;
-        rows[0] = Wg + j0 * D; rows[1] = Wu + j0 * D;
-        rows[2] = Wg + j1 * D; rows[3] = Wu + j1 * D;
-    }
-    // kept rows of W_d^T in slot order; thread tid owns columns 8 tid .. + 7
-    const uint16_t* drow[KEEP];
-    {
-        uint64_t m = sel;
+        uint64_t m = drop(sel, DPH * hf);
 #pragma unroll
-        for (int k = 0; k < KEEP; ++k) {
-            drow[k] = WdT + ((size_t)b * kBank + __builtin_ctzll(m)) * D + 8 * tid;
+        for (int k = 0; k < DPH; ++k) {
+            drow[k] = WdT + ((size_t)b * kBank + __builtin_ctzll(m)) * D + col;
             m &= m - 1;
         }
     }
-    // the ordered load stream: step s < NCX fetches chunk s of the four
-    // gate/up rows, step NCX + q the W_d^T pieces 4 q .. 4 q + 3
-    Raw<uint16_t> rc[NCX][4];
-    Raw<uint16_t> rd[KEEP];
+    // the ordered load stream: step s < NCX / 2 fetches chunks 2 s and 2 s + 1
+    // of both gate/up rows, step NCX / 2 + q the W_d^T pieces 4 q .. 4 q + 3
+    Raw<uint16_t> rc[NCX][2];
+    Raw<uint16_t> rd[DPH];
     auto issue = [&](int st) {
-        if (st < NCX) {
+        if (st < NCX / 2) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) rc[st][k].load_stream(rows[k] + 8 * (lane + kWave * st));
-        } else if (st < NCX + KEEP / 4) {
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) rd[4 * (st - NCX) + k].load_stream(drow[4 * (st - NCX) + k]);
+                for (int k = 0; k < 2; ++k)
+                    rc[2 * st + h][k].load_stream(rows[k] + 8 * (lane + kWave * (2 * st + h)));
+        } else if (st < NS) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rd[4 * (st - NCX / 2) + k].load_stream(drow[4 * (st - NCX / 2) + k]);
         }
     };
 #pragma unroll
     for (int st = 0; st < kFusedAhead; ++st) issue(st);
-    float u0 = 0.f, v0 = 0.f, u1 = 0.f, v1 = 0.f;
+    float u = 0.f, v = 0.f;
 #pragma unroll
-    for (int m = 0; m < NCX; ++m) {
+    for (int st = 0; st < NCX / 2; ++st) {
         // the scheduling barriers keep each step's loads behind the previous
         // step's arithmetic, so that the window stays bounded
         __builtin_amdgcn_sched_barrier(0);
-        const uint4 xw = xs[lane + kWave * m];
-        const float xv[8] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y),
-                             bf16_lo(xw.z), bf16_hi(xw.z), bf16_lo(xw.w), bf16_hi(xw.w)};
-        float g0[8], q0[8], g1[8], q1[8];
-        rc[m][0].decode(g0);
-        rc[m][1].decode(q0);
-        rc[m][2].decode(g1);
-        rc[m][3].decode(q1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            u0 = fmaf(xv[e], g0[e], u0);
-            v0 = fmaf(xv[e], q0[e], v0);
-            u1 = fmaf(xv[e], g1[e], u1);
-            v1 = fmaf(xv[e], q1[e], v1);
+        for (int h = 0; h < 2; ++h) {
+            const int m = 2 * st + h;
+            const uint4 xw = xs[lane + kWave * m];
+            const float xv[8] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y),
+                                 bf16_lo(xw.z), bf16_hi(xw.z), bf16_lo(xw.w), bf16_hi(xw.w)};
+            float g[8], q[8];
+            rc[m][0].decode(g);
+            rc[m][1].decode(q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u = fmaf(xv[e], g[e], u);
+                v = fmaf(xv[e], q[e], v);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue(m + kFusedAhead);
+        issue(st + kFusedAhead);
     }
 #pragma unroll
-    for (int st = NCX + kFusedAhead; st < NCX + KEEP / 4; ++st) issue(st);
+    for (int st = NCX / 2 + kFusedAhead; st < NS; ++st) issue(st);
     __builtin_amdgcn_sched_barrier(0);
     {
-        const float a0 = wave_sum(u0), b0 = wave_sum(v0), a1 = wave_sum(u1), b1 = wave_sum(v1);
+        const float a0 = wave_sum(u), b0 = wave_sum(v);
         if (lane == 0) {
             const float p0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), c0));
-            const float p1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), c1));
             sh[wv] = (gate ? sigmoidf_dev(a0) : sigmoidf_dev(p0)) * a0 * b0;
-            sh[wv + NW] = (gate ? sigmoidf_dev(a1) : sigmoidf_dev(p1)) * a1 * b1;
         }
     }
     __syncthreads();
 
-    // this bank's share of y over all columns
+    // this bank's share of y over all columns, half of the kept rows per
+    // thread group; the upper half's sums go through LDS
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
-    for (int k = 0; k < KEEP; ++k) {
-        const float hk = sh[k];
+    for (int k = 0; k < DPH; ++k) {
+        const float hk = sh[DPH * hf + k];
         float w8[8];
         rd[k].decode(w8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = fmaf(hk, w8[e], o[e]);
     }
-    float* out = partial + ((size_t)t * nb + b) * D + 8 * tid;
-    reinterpret_cast<float4*>(out)[0] = make_float4(o[0], o[1], o[2], o[3]);
-    reinterpret_cast<float4*>(out)[1] = make_float4(o[4], o[5], o[6], o[7]);
+    if (hf == 1) {
+        comb[tid - CPT][0] = make_float4(o[0], o[1], o[2], o[3]);
+        comb[tid - CPT][1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
+    __syncthreads();
+    if (hf == 0) {
+        const float4 q0 = comb[tid][0], q1 = comb[tid][1];
+        float* out = partial + ((size_t)t * nb + b) * D + col;
+        reinterpret_cast<float4*>(out)[0] = make_float4(o[0] + q0.x, o[1] + q0.y, o[2] + q0.z, o[3] + q0.w);
+        reinterpret_cast<float4*>(out)[1] = make_float4(o[4] + q1.x, o[5] + q1.y, o[6] + q1.z, o[7] + q1.w);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -595,7 +609,7 @@ static hipError_t gather_forward(const GatherArgs& a, hipStream_t s) {
                     static_cast<const E*>(a.A), a.z, a.d, a.rank, rb);
         if constexpr (sizeof(E) == 2) {
             if (fused_ok(a)) {
-                xlaunch(a.events, 1, k_bank_fused<16>, dim3((unsigned)(T * nb)), dim3(512), 0, s, x, a.z,
+                xlaunch(a.events, 1, k_bank_fused<16>, dim3((unsigned)(T * nb)), dim3(64 * 16), 0, s, x, a.z,
                         static_cast<const E*>(a.B), a.bias, static_cast<const E*>(a.W_g),
                         static_cast<const E*>(a.W_u), static_cast<const E*>(a.W_dT), a.rank, a.d_i,
                         a.gate, a.mask, a.logits, a.partial);
