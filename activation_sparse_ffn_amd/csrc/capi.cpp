@@ -542,7 +542,8 @@ const char* sparse_ffn_stage_name(sffn_handle_t h, int64_t T, int32_t i) {
     if (dense_silu && i < (use_gather(h->cfg, T) ? 2 : 3)) return "none";
     if (!use_gather(h->cfg, T)) {
         const sffn_config_t& c = h->cfg;
-        const bool fused = !use_skinny(c, T) && sffn::mfma_fused_topk(T, c.d, c.d_i, c.rank);
+        // the skinny path (4 < T <= 64) always ranks in the predictor GEMM's epilogue
+        const bool fused = use_skinny(c, T) || sffn::mfma_fused_topk(T, c.d, c.d_i, c.rank);
         return fused ? mfma_fused[i] : mfma[i];
     }
     sffn::GatherArgs a{};

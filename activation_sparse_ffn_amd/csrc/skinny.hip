@@ -234,6 +234,130 @@ __global__ __launch_bounds__(256) void k_skinny(const SkinnyParams p) {
         }
 }
 
+// Predictor layer 2 with the bank top-k in its epilogue: one workgroup of
+// eight waves per bank computes the bank's M x 64 logits (+ bias) -- the
+// waves take the rank's 64-wide K steps in turn, each step fetched like
+// k_skinny's (two 32-row weight tiles and the token tiles) -- and after the
+// waves' partial sums meet in LDS, one wave ranks them, lane t selecting
+// token t's kept channels (lane_select64): the mask words, the or of the
+// batch's mask words (the union) and the fp32 logits, which the gate/up
+// epilogue reads for sigmoid(p).
+template <int MT>
+__global__ __launch_bounds__(512) void k_skinny_topk(const SkinnyParams p, int keep, uint64_t* __restrict__ mask) {
+    constexpr int NW = 8, NB = 2, NT = NB + MT;
+    constexpr int TILE = 32 * 128;                          // bytes per operand tile
+    constexpr int STAGE = NW * NT * TILE;                   // every wave's staging tiles
+    constexpr int RED = NW * NB * MT * 16 * kWave * 4;      // the waves' partial sums
+    constexpr int PITCH = kBank * 4 + 16;                   // bytes per token row of the logit tile
+    constexpr int LGT = 32 * MT * PITCH;
+    __shared__ __attribute__((aligned(16))) char smem[STAGE > RED + LGT ? STAGE : RED + LGT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bank = blockIdx.x, n0 = bank * kBank;
+    const int steps = p.K / 64;
+    char* stage = smem + wv * NT * TILE;
+
+    // global fetch pattern: instruction q, lane l -> row 8 q + l / 8, chunk l % 8
+    const int fr = lane >> 3, fc = lane & 7;
+    const uint16_t* src[NT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) src[b] = p.B0 + (size_t)(n0 + 32 * b + fr) * p.K + 8 * fc;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) src[NB + mt] = p.A + (size_t)(mt * 32 + fr) * p.K + 8 * fc;
+    const size_t rstride8 = (size_t)8 * p.K;
+
+    f32x16 acc[NB][MT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[b][mt][v] = 0.f;
+    const int r = lane & 31, h = lane >> 5;
+    for (int st = wv; st < steps; st += NW) {
+        uint4 w[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t* at = src[t] + q * rstride8 + 64 * st;
+                if (t < NB) {
+                    w[t][q] = *reinterpret_cast<const uint4*>(at);
+                } else {
+                    const bool valid = (t - NB) * 32 + 8 * q + fr < p.M;   // rows past M: zero
+                    w[t][q] = valid ? *reinterpret_cast<const uint4*>(at) : make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint4*>(stage + t * TILE + tile_off(8 * q + fr, fc)) = w[t][q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x8 fb[NB], fa[MT];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                fb[b] = *reinterpret_cast<const bf16x8*>(stage + b * TILE + tile_off(r, 4 * h + i));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                fa[mt] = *reinterpret_cast<const bf16x8*>(stage + (NB + mt) * TILE + tile_off(r, 4 * h + i));
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[b][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[b], acc[b][mt], 0, 0, 0);
+        }
+    }
+
+    // the waves' partial sums meet in LDS; wave w finishes elements
+    // v = 2 w, 2 w + 1 of every accumulator tile into the logit tile
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);          // [NW][NB * MT * 16][64]
+    char* const lg = smem + RED;                          // [32 MT][PITCH]
+    auto R = [&](int wave, int e, int ln) -> float& { return red[((size_t)wave * NB * MT * 16 + e) * kWave + ln]; };
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) R(wv, (b * MT + mt) * 16 + v, lane) = acc[b][mt][v];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int v = 2 * wv + q;
+                const int m = mt * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
+                const int e = (b * MT + mt) * 16 + v;
+                float val = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) val += R(w2, e, lane);
+                const int c = 32 * b + r;
+                val += p.bias ? p.bias[n0 + c] : 0.f;
+                *reinterpret_cast<float*>(lg + m * PITCH + 4 * c) = val;
+                if (m < p.M) p.Cf[(size_t)m * p.N + n0 + c] = val;
+            }
+    __syncthreads();
+    if (wv != 0) return;
+    // lane t ranks token t (lanes past M repeat the last token and add
+    // nothing to the union)
+    const int t = lane < p.M ? lane : p.M - 1;
+    const char* row = lg + t * PITCH;
+    const uint64_t sel =
+        lane_select64([&](int c) { return *reinterpret_cast<const float4*>(row + 16 * c); }, keep);
+    if (lane < p.M) mask[(size_t)lane * (p.N / kBank) + bank] = sel;
+    uint32_t lo = lane < p.M ? (uint32_t)sel : 0u, hi = lane < p.M ? (uint32_t)(sel >> 32) : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo |= (uint32_t)__shfl_xor((int)lo, o, kWave);
+        hi |= (uint32_t)__shfl_xor((int)hi, o, kWave);
+    }
+    if (lane == 0 && p.unionw) p.unionw[bank] = ((uint64_t)hi << 32) | lo;
+}
+
 // The down projection Y = H W_d^T with W_d^T K-major ([K = d_i][N = d]): a
 // workgroup owns 64 columns of Y (128-byte pieces of 64 consecutive K-rows
 // per K step: whole cache lines) and a K range; its four waves take
@@ -477,13 +601,14 @@ hipError_t launch_skinny_forward(const MfmaArgs& a, float* partial, hipStream_t 
                 sum_bf16(partial, a.z, sp, (int64_t)M * a.rank, s, a.events, 0);
             }
         }
-        // P = Z B^T + bias
+        // P = Z B^T + bias, the bank top-k (mask words and union) in the epilogue
         p = SkinnyParams{};
         p.A = a.z; p.B0 = a.B; p.M = M; p.N = a.d_i; p.K = a.rank; p.Cf = a.logits; p.bias = a.bias;
-        skinny<SK_F32_BIAS, 1>(p, 1, s, a.events, 1, true);
-        // mask
-        const hipError_t e = launch_bank_topk(a.logits, a.T, a.d_i, a.keep, a.mask, nullptr, s, a.events, 2, unionw);
-        if (e != hipSuccess) return e;
+        p.unionw = unionw;
+        const dim3 grid((unsigned)(a.d_i / kBank));
+        if (M <= 32) xlaunch(a.events, 1, k_skinny_topk<1>, grid, dim3(512), 0, s, p, a.keep, a.mask);
+        else xlaunch(a.events, 1, k_skinny_topk<2>, grid, dim3(512), 0, s, p, a.keep, a.mask);
+        skip_range(a.events, 2, 3, s);
     }
     // H = select(m, s u v, 0)
     p = SkinnyParams{};
