@@ -76,12 +76,9 @@ inline size_t gate_tiles_bytes(int64_t T, int d_i, int keep, int gate) {
 }
 
 // ---- bank top-k of fp32 logits [T, d_i]: mask words, optional kept ids ------
-// union_out (d_i / 64 words) or null: receives the or of the T tokens' mask
-// words of each bank (T <= 64, no ids)
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s,
-                            void* const* events = nullptr, int stage = 0,
-                            uint64_t* union_out = nullptr);
+                            void* const* events = nullptr, int stage = 0);
 
 // ---- token-gather path (VALU; decode and fp32 layers) ---------------------
 struct GatherArgs {

@@ -39,29 +39,6 @@ __global__ __launch_bounds__(256) void k_bank_topk(const float* __restrict__ log
     }
 }
 
-// A small batch (T <= 64 tokens): one wave per bank, lane t ranking token t
-// (lane_select64 over the token's 64 logits of the bank), so that the
-// batch's union word of the bank is an or across the wave's lanes.
-constexpr int kUnionMaxTokens = 64;
-__global__ __launch_bounds__(256) void k_bank_topk_union(const float* __restrict__ logits, int T, int nb,
-                                                         int keep, uint64_t* __restrict__ mask,
-                                                         uint64_t* __restrict__ unionw) {
-    const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (b >= nb) return;
-    const int t = lane < T ? lane : T - 1;         // lanes past T repeat the last token
-    const float* row = logits + ((int64_t)t * nb + b) * kBank;
-    const uint64_t sel = lane_select64([&](int c) { return reinterpret_cast<const float4*>(row)[c]; }, keep);
-    if (lane < T) mask[(int64_t)lane * nb + b] = sel;
-    uint32_t lo = (uint32_t)sel, hi = (uint32_t)(sel >> 32);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        lo |= (uint32_t)__shfl_xor((int)lo, o, kWave);
-        hi |= (uint32_t)__shfl_xor((int)hi, o, kWave);
-    }
-    if (lane == 0) unionw[b] = ((uint64_t)hi << 32) | lo;
-}
-
 // Many banks: one bank per lane. Each wave is a workgroup of its own and
 // walks chunks of 64 consecutive (token, bank) words (16 KB), chunk c, c +
 // n_waves, ...: a chunk's logits go from global memory straight into the
@@ -207,14 +184,9 @@ static int compute_units() {
 
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s, void* const* events,
-                            int stage, uint64_t* union_out) {
+                            int stage) {
     const int nb = d_i / kBank;
     const int64_t n_words = T * nb;
-    if (union_out != nullptr && T <= kUnionMaxTokens && ids == nullptr) {
-        xlaunch(events, stage, k_bank_topk_union, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, s, logits, (int)T, nb,
-                keep, mask, union_out);
-        return hipGetLastError();
-    }
     if (n_words >= 65536) {
         const int n_cu = compute_units();
         const int64_t chunks = (n_words + kWave - 1) / kWave;

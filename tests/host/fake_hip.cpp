@@ -45,8 +45,7 @@ static hipError_t launched() {
     return g_fake_launch_status;
 }
 hipError_t launch_fill_mask(uint64_t*, int64_t, hipStream_t) { return launched(); }
-hipError_t launch_bank_topk(const float*, int64_t, int, int, uint64_t*, uint16_t*, hipStream_t, void* const*, int,
-                            uint64_t*) {
+hipError_t launch_bank_topk(const float*, int64_t, int, int, uint64_t*, uint16_t*, hipStream_t, void* const*, int) {
     return launched();
 }
 int gather_groups(int d_s) { return (d_s + 63) / 64; }
