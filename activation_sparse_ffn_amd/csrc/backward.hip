@@ -31,23 +31,19 @@
 
 namespace sffn {
 
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
 
-// One workgroup per (block of 64 tokens, bank): each wave takes 16 of the
-// tokens in turn, one channel per lane. g_u, g_v and g_p leave token-major
-// (the A operands of g_x and g_z); h, g_u, g_v and g_p also leave transposed
-// through LDS, [d_i][Tp] with zero columns past T (the operands of the
-// weight gradients, which contract over tokens); g_p's column sums over the
-// block go to colpart[block][d_i] for g_bias.
+// One workgroup per (block of 64 tokens, bank). Thread (token row tid / 8,
+// chunk tid % 8) takes channels 8 c .. 8 c + 7 of one token per pass (two
+// passes of 32 tokens), so every load and store moves 16 bytes (p 32 bytes);
+// the bank's threshold comes from a reduction over the token's 8 lanes. g_u,
+// g_v and g_p leave token-major (the A operands of g_x and g_z); h, g_u, g_v
+// and g_p also leave transposed through LDS, [d_i][Tp] with zero columns past
+// T (the operands of the weight gradients, which contract over tokens); g_p's
+// column sums over the block, in a fixed order, go to colpart[block][d_i] for
+// g_bias. In the LDS tiles ([channel][token], 128-byte rows) the 16-byte
+// chunk of tokens 8 k .. 8 k + 7 of channel row ch sits at slot
+// k ^ ((ch >> 3) & 7), so that the 8 lanes of one token, whose channels are 8
+// rows apart, write to different banks.
 constexpr int kBwdTok = 64;
 __global__ __launch_bounds__(256) void k_bwd_tile(const float* __restrict__ p, const uint16_t* __restrict__ U,
                                                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ g_h,
@@ -57,66 +53,105 @@ __global__ __launch_bounds__(256) void k_bwd_tile(const float* __restrict__ p, c
                                                   uint16_t* __restrict__ g_p16, uint16_t* __restrict__ hT,
                                                   uint16_t* __restrict__ guT, uint16_t* __restrict__ gvT,
                                                   uint16_t* __restrict__ gpT, float* __restrict__ colpart) {
-    constexpr int LD = kBwdTok + 8;                  // row pitch (elements) of the LDS tiles: 144 bytes
-    __shared__ __attribute__((aligned(16))) uint16_t tile[4][kBank][LD];
-    __shared__ float csum[4][kBank];
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int ROWS = 256 / 8;                    // tokens per pass
+    __shared__ __attribute__((aligned(16))) uint16_t tile[4][kBank][kBwdTok];
+    __shared__ float csum[ROWS][kBank + 1];
+    const int tid = threadIdx.x;
+    const int c8 = tid & 7, tr = tid >> 3;
     const int tb = blockIdx.x, b = blockIdx.y;
     const int d_i = nb * kBank;
-    const int j = b * kBank + lane;
-    float colp = 0.f;
-    for (int i = 0; i < kBwdTok / 4; ++i) {
-        const int tl = wv * (kBwdTok / 4) + i;       // token within the block
+    const int j0 = b * kBank + 8 * c8;               // this thread's first channel
+    auto slot = [](int ch, int tl) { return (((tl >> 3) ^ ((ch >> 3) & 7)) << 3) + (tl & 7); };
+    float colp[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) colp[e] = 0.f;
+#pragma unroll
+    for (int pass = 0; pass < kBwdTok / ROWS; ++pass) {
+        const int tl = tr + ROWS * pass;             // token within the block
         const int64_t t = (int64_t)tb * kBwdTok + tl;
-        uint16_t o_h = 0, o_u = 0, o_v = 0, o_p = 0;
-        if (t < T) {
-            const int64_t w = t * nb + b;
-            const int64_t o = t * (int64_t)d_i + j;
-            const float pv = p[o], u = bf16_to_f32(U[o]), v = bf16_to_f32(V[o]), gh = bf16_to_f32(g_h[o]);
-            const bool kept = (mask[w] >> lane) & 1ull;
-            const float m = kept ? 1.f : 0.f;
+        uint16_t oh[8], ou[8], ov[8], op[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oh[e] = ou[e] = ov[e] = op[e] = 0;
+        if (t < T) {                                 // the same for the token's 8 lanes
+            const int64_t o = t * (int64_t)d_i + j0;
+            const float4 p0 = *reinterpret_cast<const float4*>(p + o);
+            const float4 p1 = *reinterpret_cast<const float4*>(p + o + 4);
+            Raw<uint16_t> ru, rv, rg;
+            ru.load(U + o); rv.load(V + o); rg.load(g_h + o);
+            const uint64_t mw = mask[t * nb + b];
+            const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            float u[8], v[8], gh[8];
+            ru.decode(u); rv.decode(v); rg.decode(gh);
             // threshold: midpoint of the smallest kept and the largest dropped logit
-            const float key = __builtin_isnan(pv) ? -__builtin_huge_valf() : pv;
-            const float kmin = wave_min(kept ? key : __builtin_huge_valf());
-            const float dmax = wave_max(kept ? -__builtin_huge_valf() : key);
-            const float sp = sigmoidf_dev(pv), su = sigmoidf_dev(u);
-            const float s = gate ? su : sp;
-            const float gm = gh * s * u * v;                 // dL/dm
-            const float gu = gate ? m * gh * v * (su + u * su * (1.f - su)) : m * gh * s * v;
-            const float gv = m * gh * s * u;
-            float gp = gate ? 0.f : m * gh * u * v * sp * (1.f - sp);
-            if (keep < kBank && inv_tau > 0.f) {
-                const float theta = 0.5f * (kmin + dmax);
-                const float sa = sigmoidf_dev((pv - theta) * inv_tau);
-                gp += gm * sa * (1.f - sa) * inv_tau;
+            float kmin = __builtin_huge_valf(), dmax = -__builtin_huge_valf();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float key = __builtin_isnan(pv[e]) ? -__builtin_huge_valf() : pv[e];
+                const bool kept = (mw >> (8 * c8 + e)) & 1ull;
+                kmin = kept ? fminf(kmin, key) : kmin;
+                dmax = kept ? dmax : fmaxf(dmax, key);
             }
-            colp += gp;
-            o_h = f32_to_bf16(m * s * u * v);
-            o_u = f32_to_bf16(gu);
-            o_v = f32_to_bf16(gv);
-            o_p = f32_to_bf16(gp);
-            g_u[o] = o_u;
-            g_v[o] = o_v;
-            g_p16[o] = o_p;
+#pragma unroll
+            for (int o2 = 1; o2 < 8; o2 <<= 1) {
+                kmin = fminf(kmin, __shfl_xor(kmin, o2, kWave));
+                dmax = fmaxf(dmax, __shfl_xor(dmax, o2, kWave));
+            }
+            const float theta = 0.5f * (kmin + dmax);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool kept = (mw >> (8 * c8 + e)) & 1ull;
+                const float m = kept ? 1.f : 0.f;
+                const float sp = sigmoidf_dev(pv[e]), su = sigmoidf_dev(u[e]);
+                const float sg = gate ? su : sp;
+                const float gm = gh[e] * sg * u[e] * v[e];   // dL/dm
+                const float gu = gate ? m * gh[e] * v[e] * (su + u[e] * su * (1.f - su)) : m * gh[e] * sg * v[e];
+                const float gv = m * gh[e] * sg * u[e];
+                float gp = gate ? 0.f : m * gh[e] * u[e] * v[e] * sp * (1.f - sp);
+                if (keep < kBank && inv_tau > 0.f) {
+                    const float sa = sigmoidf_dev((pv[e] - theta) * inv_tau);
+                    gp += gm * sa * (1.f - sa) * inv_tau;
+                }
+                colp[e] += gp;
+                oh[e] = f32_to_bf16(m * sg * u[e] * v[e]);
+                ou[e] = f32_to_bf16(gu);
+                ov[e] = f32_to_bf16(gv);
+                op[e] = f32_to_bf16(gp);
+            }
+            auto pack = [](const uint16_t (&h)[8]) {
+                return make_uint4((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                                  (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16));
+            };
+            *reinterpret_cast<uint4*>(g_u + o) = pack(ou);
+            *reinterpret_cast<uint4*>(g_v + o) = pack(ov);
+            *reinterpret_cast<uint4*>(g_p16 + o) = pack(op);
         }
-        tile[0][lane][tl] = o_h;
-        tile[1][lane][tl] = o_u;
-        tile[2][lane][tl] = o_v;
-        tile[3][lane][tl] = o_p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ch = 8 * c8 + e;
+            const int sl = slot(ch, tl);
+            tile[0][ch][sl] = oh[e];
+            tile[1][ch][sl] = ou[e];
+            tile[2][ch][sl] = ov[e];
+            tile[3][ch][sl] = op[e];
+        }
     }
-    csum[wv][lane] = colp;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) csum[tr][8 * c8 + e] = colp[e];
     __syncthreads();
-    if (wv == 0) colpart[(size_t)tb * d_i + j] = (csum[0][lane] + csum[1][lane]) + (csum[2][lane] + csum[3][lane]);
+    if (tid < kBank) {
+        float sum = 0.f;
+        for (int r = 0; r < ROWS; ++r) sum += csum[r][tid];
+        colpart[(size_t)tb * d_i + b * kBank + tid] = sum;
+    }
     // transposed tiles: 64 channel rows of 128 bytes per output, 16 bytes per thread
     uint16_t* const dst[4] = {hT, guT, gvT, gpT};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int c = threadIdx.x + 256 * k;            // 512 chunks: row c / 8, chunk c % 8
+            const int c = tid + 256 * k;             // 512 chunks: row c / 8, chunk c % 8
             const int row = c >> 3, ch = c & 7;
-            const uint4 val = *reinterpret_cast<const uint4*>(&tile[q][row][8 * ch]);
+            const uint4 val = *reinterpret_cast<const uint4*>(&tile[q][row][(ch ^ ((row >> 3) & 7)) << 3]);
             *reinterpret_cast<uint4*>(dst[q] + (size_t)(b * kBank + row) * Tp + (size_t)tb * kBwdTok + 8 * ch) = val;
         }
     }
