@@ -378,7 +378,7 @@ void k_bank_fused(const uint16_t* __restrict__ x, const float* __restrict__ z,
     for (int c = lane; c < nch; c += kWave) {
         Raw<uint16_t> rb[RPW];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) rb[i].load(B + (row0 + i) * rank + 8 * c);
+        for (int i = 0; i < RPW; ++i) rb[i].load_stream(B + (row0 + i) * rank + 8 * c);   // read once per token
         const float* zt = z + (size_t)t * rank + 8 * c;
         const float4 z0 = *reinterpret_cast<const float4*>(zt);
         const float4 z1 = *reinterpret_cast<const float4*>(zt + 4);
