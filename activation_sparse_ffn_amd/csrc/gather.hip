@@ -682,10 +682,47 @@ __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ src, E*
     }
 }
 
+// The same for bf16 with 16-byte global accesses (cols and ld multiples of 8,
+// 16-byte aligned pointers): a thread moves 8 consecutive elements of a
+// source row into LDS and later gathers 8 rows of one column from it.
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     int rows, int cols, int ld) {
+    constexpr int P = 64 + 2;                        // row pitch (elements): 132 bytes
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int q = threadIdx.x + 256 * k, r = q >> 3, cc = 8 * (q & 7);
+        const int gr = r0 + r, gc = c0 + cc;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (gr < rows && gc < cols) v = *reinterpret_cast<const uint4*>(src + (int64_t)gr * cols + gc);
+        uint32_t* t32 = reinterpret_cast<uint32_t*>(tile + r * P + cc);
+        t32[0] = v.x; t32[1] = v.y; t32[2] = v.z; t32[3] = v.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int q = threadIdx.x + 256 * k, c = q >> 3, rr = 8 * (q & 7);
+        const int gc = c0 + c, gr = r0 + rr;
+        if (gc >= cols || gr >= ld) continue;
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = tile[(rr + i) * P + c];
+        *reinterpret_cast<uint4*>(dst + (int64_t)gc * ld + gr) =
+            make_uint4((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16),
+                       (uint32_t)e[4] | ((uint32_t)e[5] << 16), (uint32_t)e[6] | ((uint32_t)e[7] << 16));
+    }
+}
+
 hipError_t launch_transpose(Dt dt, const void* src, void* dst, int rows, int cols, hipStream_t s, int ld) {
     if (ld < rows) ld = rows;
     dim3 grid((cols + 63) / 64, (ld + 63) / 64);
-    if (dt == Dt::BF16)
+    const bool wide = dt == Dt::BF16 && cols % 8 == 0 && ld % 8 == 0 &&
+                      (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    if (wide)
+        hipLaunchKernelGGL(k_transpose16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src),
+                           static_cast<uint16_t*>(dst), rows, cols, ld);
+    else if (dt == Dt::BF16)
         hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s,
                            static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows, cols, ld);
     else
