@@ -447,9 +447,18 @@ constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
 
 
-template <int EPI, int WN, bool KMAJOR = false>
+// PERSIST (gate/up with gate tiles only): the grid is one workgroup per
+// compute unit and workgroup g walks tiles g, g + G, g + 2 G, ... (G, the
+// grid size, a multiple of 8, so every tile of a workgroup falls on the XCD
+// that its number gives). When the epilogue has expanded a compact gate tile
+// out of slab buffer 0, it requests the next tile's first slab into that
+// buffer, so that the load's latency passes under the rest of the epilogue
+// (the gate values, the H tile and its stores) instead of opening the next
+// tile with an idle wait.
+template <int EPI, int WN, bool KMAJOR = false, bool PERSIST = false>
 __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_tiles, int n_tiles) {
     static_assert(!KMAJOR || EPI == EPI_BF16, "a K-major B only for the plain bf16 GEMM");
+    static_assert(!PERSIST || EPI == EPI_GATEUP, "persistent tiles only for gate/up");
     // WN waves along N (2 or 4), 2 along M: each wave owns 128 x (256 / WN) of C
     constexpr bool GU = EPI == EPI_GATEUP || EPI == EPI_AMP || EPI == EPI_UV;   // B = [W_g, W_u] blocks
     constexpr int NT = 128 * WN;                     // threads
@@ -458,7 +467,11 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     constexpr int GB = WNC / 2;                       // gate/up interleave block (rows)
     constexpr int NF = TM * 8 / NT;                   // 16-byte fetches per thread per operand
     constexpr int TNC = GU ? TN / 2 : TN;             // output columns per tile
-    const int tid = threadIdx.x, lane = tid & 63;
+    // tid is opaque again at the top of each persistent tile (below), so that
+    // what the epilogue and the gate-tile fetch derive from it is computed per
+    // tile rather than held, or spilled, across the K loop
+    int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WN, wn = wv % WN;
     const int r32 = lane & 31, hk = lane >> 5;
@@ -473,16 +486,22 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
     // misses per K step by a third. Every 256 x 256 tile streams 64 KB per K
     // step through its compute unit, and the misses' latency is what limits
     // how fast that stream flows.
-    const unsigned total = gridDim.x, g = blockIdx.x;
-    const unsigned gx = (total % 8 == 0) ? (g % 8) * (total / 8) + g / 8 : g;
+    const unsigned total = (unsigned)(m_tiles * n_tiles);
     constexpr int GM = 8;
-    const int grp = (int)(gx / (unsigned)(GM * n_tiles));
-    const int first_m = grp * GM;
-    const int gm = min(m_tiles - first_m, GM);
-    const int within = (int)(gx - (unsigned)grp * (unsigned)(GM * n_tiles));
-    const int mt = first_m + within % gm, nt = within / gm;
-    const int64_t m0 = (int64_t)mt * TM;
-    const int n0 = nt * TNC;
+    auto place = [&](unsigned g, int& mt, int& nt) {
+        const unsigned gx = (total % 8 == 0) ? (g % 8) * (total / 8) + g / 8 : g;
+        const int grp = (int)(gx / (unsigned)(GM * n_tiles));
+        const int first_m = grp * GM;
+        const int gm = min(m_tiles - first_m, GM);
+        const int within = (int)(gx - (unsigned)grp * (unsigned)(GM * n_tiles));
+        mt = first_m + within % gm;
+        nt = within / gm;
+    };
+    unsigned tile = blockIdx.x;
+    int mt, nt;
+    place(tile, mt, nt);
+    int64_t m0 = (int64_t)mt * TM;
+    int n0 = nt * TNC;
 
     // per-thread fetch rows: chunk c = tid + NT i -> row c / 8, slot c % 8.
     // Gate/up B rows come in blocks of GB: [W_g, W_u] for channels n0 + GB b ..
@@ -623,7 +642,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
             char* const er = dst + row * 256 + bsel * 128;
 #pragma unroll
             for (int c = 0; c < 8; ++c)     // rotated by lane: neighbours start on different banks
-                *reinterpret_cast<uint4*>(er + 16 * ((c + lane) & 7)) =
+                *reinterpret_cast<uint4*>(er + 16 * ((c + tid) & 7)) =
                     make_uint4(dropped2, dropped2, dropped2, dropped2);
             // 16 kept channels at a time: their positions (one 16-byte
             // chunk) and values (two), requested together
@@ -661,166 +680,230 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
         interleave();
     };
 
-    sources(m0, n0);
-    gtile = gate_tile(mt, nt);
-    compact = gtile != nullptr && gate_compact(p.keep);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    fetch(0, buf0);
-    landed();
-    if (kt_n > 1) fetch(TK, buf1);
-    frags(buf0, 0, xa, xb);
-    int kt = 0;
-    for (; kt + 2 <= kt_n; kt += 2) {
-        step(buf0, buf1, kt);
-        step(buf1, buf0, kt + 1);
-    }
-    if (kt < kt_n) step(buf0, buf1, kt);       // odd count: the last slab is in buf0
-    // the gate tile went into the second-to-last step's `cur`, which is the
-    // last step's `nxt` (one step only: that step's `cur`, buf0)
-    char* gbuf = kt_n == 1 ? buf0 : ((kt_n & 1) ? buf1 : buf0);
-
-    // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2)
-    // + 4 (lane >> 5); for gate/up, tile j < NJ / 2 holds u and tile
-    // j + NJ / 2 holds v of channels n0 + wn GB + 32 j + (lane & 31)
-    if constexpr (EPI == EPI_AMP) {
-        // Dense-4x baseline: a = SiLU(u) v of the 256 x 128 block goes to LDS
-        // (both freed slab buffers) as 512 bank-rows q = 2 row + (col >> 6)
-        // of 256 bytes, 16-byte chunks swizzled by q; thread q then ranks
-        // |a| of its bank-row and writes the mask word, the masked bf16 h
-        // and, when asked for, the amplitudes
-        landed();
-        auto arow = [&](int q) { return (q < 256 ? buf0 : buf1) + (q & 255) * 256; };
+    // PERSIST: one pass per tile of the workgroup; otherwise one pass
+    bool primed = false;    // the next tile's sources and first slab are requested
+    for (bool first = true;; first = false) {
+        if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+        if (!first) {
+            tile += gridDim.x;
+            if (tile >= total) return;
+            place(tile, mt, nt);
+            m0 = (int64_t)mt * TM;
+            n0 = nt * TNC;
+        }
+        if (primed) {
+            primed = false;               // sources and slab 0 already requested
+        } else {
+            sources(m0, n0);
+            if (!first) __syncthreads();  // the previous tile's epilogue is done with buffer 0
+            fetch(0, buf0);
+        }
+        gtile = gate_tile(mt, nt);
+        compact = PERSIST || (gtile != nullptr && gate_compact(p.keep));   // PERSIST: launched for compact tiles
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int j = 0; j < NJ / 2; ++j) {
-                    const int col = wn * GB + j * 32 + r32;
-                    const int q = 2 * rt + (col >> 6), c64 = col & 63;
-                    const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
-                    *reinterpret_cast<float*>(arow(q) + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
-                        sigmoidf_dev(u) * u * vv;
-                }
-            }
-        __syncthreads();
-        const int q = tid;                               // NT = 512 bank-rows
-        const int64_t t = m0 + (q >> 1);
-        const int j0 = n0 + (q & 1) * kBank;
-        const char* r = arow(q);
-        auto ld = [&](int c) { return *reinterpret_cast<const float4*>(r + ((c ^ (q & 15)) << 4)); };
-        const uint64_t sel = lane_select64(
-            [&](int c) {
-                const float4 f = ld(c);
-                return make_float4(fabsf(f.x), fabsf(f.y), fabsf(f.z), fabsf(f.w));
-            },
-            p.keep);
-        if (t >= p.M || j0 >= p.N) return;
-        p.mask_w[t * (p.N / kBank) + j0 / kBank] = sel;
-        if (p.Cf != nullptr) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) reinterpret_cast<float4*>(p.Cf + t * p.N + j0)[c] = ld(c);
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        landed();
+        if (kt_n > 1) fetch(TK, buf1);
+        frags(buf0, 0, xa, xb);
+        int kt = 0;
+        for (; kt + 2 <= kt_n; kt += 2) {
+            step(buf0, buf1, kt);
+            step(buf1, buf0, kt + 1);
         }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float4 v0 = ld(2 * c), v1 = ld(2 * c + 1);
-            const float av[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint32_t hw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ch = 8 * c + 2 * e;
-                const uint32_t lo = ((sel >> ch) & 1ull) ? f32_to_bf16(av[2 * e]) : 0u;
-                const uint32_t hi = ((sel >> (ch + 1)) & 1ull) ? f32_to_bf16(av[2 * e + 1]) : 0u;
-                hw[e] = lo | (hi << 16);
-            }
-            *reinterpret_cast<uint4*>(p.Cb + t * p.N + j0 + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        }
-        return;
-    }
-    if constexpr (EPI == EPI_GATEUP) {
-        if (compact) {
-            // the compact gate tile, expanded into the full layout in the
-            // other slab buffer. With two or more K steps the tile landed
-            // before the last step's barrier, after which no wave reads that
-            // buffer; a single step fetched it after its barrier.
-            if (kt_n == 1) landed();
-            char* const ebuf = gbuf == buf0 ? buf1 : buf0;
-            expand(gbuf, ebuf);
-            gbuf = ebuf;
-        }
-        if (gtile != nullptr || p.dense) {
-            // H = select(kept, s u v, 0) with the gate values of the LDS
-            // copy of the gate tile, written over them in place (each
-            // element is read and written by one lane); the bf16 tile then
-            // leaves in 16-byte stores
+        if (kt < kt_n) step(buf0, buf1, kt);       // odd count: the last slab is in buf0
+        // the gate tile went into the second-to-last step's `cur`, which is the
+        // last step's `nxt` (one step only: that step's `cur`, buf0)
+        char* gbuf = kt_n == 1 ? buf0 : ((kt_n & 1) ? buf1 : buf0);
+
+        // epilogue: lane holds column (lane & 31) and rows (v & 3) + 8 (v >> 2)
+        // + 4 (lane >> 5); for gate/up, tile j < NJ / 2 holds u and tile
+        // j + NJ / 2 holds v of channels n0 + wn GB + 32 j + (lane & 31)
+        if constexpr (EPI == EPI_AMP) {
+            // Dense-4x baseline: a = SiLU(u) v of the 256 x 128 block goes to LDS
+            // (both freed slab buffers) as 512 bank-rows q = 2 row + (col >> 6)
+            // of 256 bytes, 16-byte chunks swizzled by q; thread q then ranks
+            // |a| of its bank-row and writes the mask word, the masked bf16 h
+            // and, when asked for, the amplitudes
             landed();
+            auto arow = [&](int q) { return (q < 256 ? buf0 : buf1) + (q & 255) * 256; };
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < NJ / 2; ++j) {
-                    // 16 reads in flight, then the 16 writes
-                    uint16_t* e[16];
-                    uint16_t g[16];
+                for (int v = 0; v < 16; ++v) {
+                    const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int rt = wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
-                        e[v] = reinterpret_cast<uint16_t*>(gbuf + rt * 256) + wn * GB + j * 32 + r32;
-                        g[v] = *e[v];
-                    }
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
+                    for (int j = 0; j < NJ / 2; ++j) {
+                        const int col = wn * GB + j * 32 + r32;
+                        const int q = 2 * rt + (col >> 6), c64 = col & 63;
                         const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
-                        const float sg = p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g[v]);
-                        const bool kept = p.dense || g[v] != kGateDropped;   // dense: no gate tile loaded
-                        *e[v] = kept ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                        *reinterpret_cast<float*>(arow(q) + (((c64 >> 2) ^ (q & 15)) << 4) + (c64 & 3) * 4) =
+                            sigmoidf_dev(u) * u * vv;
                     }
                 }
             __syncthreads();
+            const int q = tid;                               // NT = 512 bank-rows
+            const int64_t t = m0 + (q >> 1);
+            const int j0 = n0 + (q & 1) * kBank;
+            const char* r = arow(q);
+            auto ld = [&](int c) { return *reinterpret_cast<const float4*>(r + ((c ^ (q & 15)) << 4)); };
+            const uint64_t sel = lane_select64(
+                [&](int c) {
+                    const float4 f = ld(c);
+                    return make_float4(fabsf(f.x), fabsf(f.y), fabsf(f.z), fabsf(f.w));
+                },
+                p.keep);
+            if (t >= p.M || j0 >= p.N) return;
+            p.mask_w[t * (p.N / kBank) + j0 / kBank] = sel;
+            if (p.Cf != nullptr) {
 #pragma unroll
-            for (int i = 0; i < TM * 16 / NT; ++i) {
-                const int ch = tid + i * NT, row = ch >> 4, c16 = ch & 15;
-                const int64_t m = m0 + row;
-                const uint4 val = *reinterpret_cast<const uint4*>(gbuf + row * 256 + c16 * 16);
-                if (m < p.M) *reinterpret_cast<uint4*>(p.Cb + m * p.N + n0 + c16 * 8) = val;
+                for (int c = 0; c < 16; ++c) reinterpret_cast<float4*>(p.Cf + t * p.N + j0)[c] = ld(c);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float4 v0 = ld(2 * c), v1 = ld(2 * c + 1);
+                const float av[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ch = 8 * c + 2 * e;
+                    const uint32_t lo = ((sel >> ch) & 1ull) ? f32_to_bf16(av[2 * e]) : 0u;
+                    const uint32_t hi = ((sel >> (ch + 1)) & 1ull) ? f32_to_bf16(av[2 * e + 1]) : 0u;
+                    hw[e] = lo | (hi << 16);
+                }
+                *reinterpret_cast<uint4*>(p.Cb + t * p.N + j0 + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             }
             return;
         }
-    }
+        if constexpr (EPI == EPI_GATEUP) {
+            if (compact) {
+                // the compact gate tile, expanded into the full layout in the
+                // other slab buffer. With two or more K steps the tile landed
+                // before the last step's barrier, after which no wave reads that
+                // buffer; a single step fetched it after its barrier.
+                if (kt_n == 1) landed();
+                char* const ebuf = gbuf == buf0 ? buf1 : buf0;
+                expand(gbuf, ebuf);
+                gbuf = ebuf;
+            }
+            if (PERSIST || gtile != nullptr || p.dense) {
+                // H = select(kept, s u v, 0) with the gate values of the LDS
+                // copy of the gate tile (at hb), written over them in place
+                // (each element is read and written by one lane); the bf16
+                // tile then leaves in 16-byte stores
+                auto finish = [&](char* hb) {
+                    // LDS addresses: element (row, channel) of the tile is at
+                    // hb + 256 row + 2 channel, and the thread's 16-byte chunk
+                    // i of the H rows at hb + 256 (ch >> 4) + 16 (ch & 15),
+                    // ch = tid + NT i. The persistent kernel forms them as hb
+                    // + an opaque per-lane base + a constant: a short address
+                    // chain, along which the compiler still sees which LDS
+                    // array an access names (a chain of one GEP per addend
+                    // hides it, and each read then waits for every load in
+                    // flight into LDS, the next tile's first slab included)
+                    int eb = (wm * 128 + 4 * hk) * 256 + 2 * (wn * GB + r32);
+                    int sb = (tid >> 4) * 256 + (tid & 15) * 16;
+                    if constexpr (PERSIST) asm volatile("" : "+v"(eb), "+v"(sb));
+                    auto elem = [&](int i, int j, int v) -> uint16_t* {
+                        const int r = i * 32 + (v & 3) + 8 * (v >> 2);   // row within the wave's block
+                        if constexpr (PERSIST) return reinterpret_cast<uint16_t*>(hb + eb + (r * 256 + 64 * j));
+                        return reinterpret_cast<uint16_t*>(hb + (wm * 128 + r + 4 * hk) * 256) + wn * GB + j * 32 +
+                               r32;
+                    };
+                    auto chunk = [&](int i) -> const uint4* {
+                        if constexpr (PERSIST) return reinterpret_cast<const uint4*>(hb + sb + i * (NT / 16) * 256);
+                        const int ch = tid + i * NT;
+                        return reinterpret_cast<const uint4*>(hb + (ch >> 4) * 256 + (ch & 15) * 16);
+                    };
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < (GU ? NJ / 2 : NJ); ++j) {
-            const int n = GU ? n0 + wn * GB + j * 32 + r32 : n0 + wn * WNC + j * 32 + r32;
-            if (n >= p.N) continue;
+                        for (int j = 0; j < NJ / 2; ++j) {
+                            // 16 reads in flight, then the 16 writes
+                            uint16_t* e[16];
+                            uint16_t g[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
-                if (m >= p.M) continue;
-                const int64_t o = m * p.N + n;
-                if constexpr (EPI == EPI_BF16) {
-                    p.Cb[o] = f32_to_bf16(acc[i][j][v]);
-                } else if constexpr (EPI == EPI_F32_BIAS) {
-                    p.Cf[o] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.f);
-                } else if constexpr (EPI == EPI_F32_ACC) {
-                    p.Cf[o] += acc[i][j][v];
-                } else if constexpr (EPI == EPI_UV) {
-                    p.Cb[o] = f32_to_bf16(acc[i][j][v]);
-                    p.Cb2[o] = f32_to_bf16(acc[i][j + NJ / 2][v]);
-                } else {
-                    const float u = acc[i][j][v];
-                    const float vv = acc[i][j + NJ / 2][v];
-                    const bool keep = (p.mask[m * (p.N / kBank) + (n >> 6)] >> (n & 63)) & 1ull;
-                    const float sg = p.gate ? sigmoidf_dev(u) : sigmoidf_dev(p.P[o]);
-                    p.Cb[o] = keep ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                            for (int v = 0; v < 16; ++v) {
+                                e[v] = elem(i, j, v);
+                                g[v] = *e[v];
+                            }
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) {
+                                const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
+                                const float sg =
+                                    p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g[v]);
+                                const bool kept = p.dense || g[v] != kGateDropped;   // dense: no gate tile loaded
+                                *e[v] = kept ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                            }
+                        }
+                    // this wave's LDS writes done, then the barrier; unlike
+                    // __syncthreads it does not wait for the loads still in
+                    // flight into the other buffer (the clobber keeps the
+                    // compiler from moving memory accesses across it)
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+                    for (int i = 0; i < TM * 16 / NT; ++i) {
+                        const int ch = tid + i * NT, row = ch >> 4, c16 = ch & 15;
+                        const int64_t m = m0 + row;
+                        const uint4 val = *chunk(i);
+                        if (m < p.M) *reinterpret_cast<uint4*>(p.Cb + m * p.N + n0 + c16 * 8) = val;
+                    }
+                };
+                landed();
+                if constexpr (PERSIST) {
+                    // Launched for compact gate tiles and an even count of K
+                    // steps (or one) only, so the tile expanded out of buf0
+                    // into buf1, and buf0 is free: the next tile's first slab
+                    // goes there now. The epilogue's LDS reads name buf1
+                    // itself, so that they need not wait for those loads.
+                    primed = tile + gridDim.x < total;
+                    if (primed) {
+                        int nm, nn;
+                        place(tile + gridDim.x, nm, nn);
+                        sources((int64_t)nm * TM, nn * TNC);
+                        fetch(0, buf0);
+                    }
+                    finish(buf1);
+                    continue;
                 }
+                finish(gbuf);
+                return;
             }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < (GU ? NJ / 2 : NJ); ++j) {
+                const int n = GU ? n0 + wn * GB + j * 32 + r32 : n0 + wn * WNC + j * 32 + r32;
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = m0 + wm * 128 + i * 32 + (v & 3) + 8 * (v >> 2) + 4 * hk;
+                    if (m >= p.M) continue;
+                    const int64_t o = m * p.N + n;
+                    if constexpr (EPI == EPI_BF16) {
+                        p.Cb[o] = f32_to_bf16(acc[i][j][v]);
+                    } else if constexpr (EPI == EPI_F32_BIAS) {
+                        p.Cf[o] = acc[i][j][v] + (p.bias ? p.bias[n] : 0.f);
+                    } else if constexpr (EPI == EPI_F32_ACC) {
+                        p.Cf[o] += acc[i][j][v];
+                    } else if constexpr (EPI == EPI_UV) {
+                        p.Cb[o] = f32_to_bf16(acc[i][j][v]);
+                        p.Cb2[o] = f32_to_bf16(acc[i][j + NJ / 2][v]);
+                    } else {
+                        const float u = acc[i][j][v];
+                        const float vv = acc[i][j + NJ / 2][v];
+                        const bool keep = (p.mask[m * (p.N / kBank) + (n >> 6)] >> (n & 63)) & 1ull;
+                        const float sg = p.gate ? sigmoidf_dev(u) : sigmoidf_dev(p.P[o]);
+                        p.Cb[o] = keep ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
+                    }
+                }
+            }
+        if constexpr (!PERSIST) return;
+    }
 }
 
 #ifndef SFFN_GEMM256_WN
@@ -833,6 +916,18 @@ static void gemm256(const GemmParams& p, hipStream_t s, void* const* events, int
     const int m_tiles = (int)((p.M + TM - 1) / TM);
     constexpr int TNC = (EPI == EPI_GATEUP || EPI == EPI_AMP || EPI == EPI_UV) ? TN / 2 : TN;
     const int n_tiles = (p.N + TNC - 1) / TNC;
+    if constexpr (EPI == EPI_GATEUP) {
+        // compact gate tiles and more tiles than compute units: persistent
+        // workgroups, one per compute unit (each holds 128 KB of LDS)
+        const int n_cu = compute_units();
+        const int kt_n = p.K / TK;
+        if (p.G != nullptr && gate_compact(p.keep) && (kt_n % 2 == 0 || kt_n == 1) && m_tiles * n_tiles > n_cu &&
+            n_cu % 8 == 0) {
+            xlaunch(events, stage, k_gemm256<EPI, WN, KMAJOR, true>, dim3((unsigned)n_cu), dim3(128 * WN), 0, s,
+                    p, m_tiles, n_tiles);
+            return;
+        }
+    }
     xlaunch(events, stage, k_gemm256<EPI, WN, KMAJOR>, dim3((unsigned)(m_tiles * n_tiles)), dim3(128 * WN), 0, s,
             p, m_tiles, n_tiles);
 }

@@ -35,6 +35,21 @@ inline void skip_range(void* const* events, int from, int to, hipStream_t s) {
         (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
 }
 
+// Compute units of the current device, asked once per device (every thread
+// that races on the first call stores the same value).
+inline int compute_units() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
 // Every channel kept: n_words mask words of all ones.
 hipError_t launch_fill_mask(uint64_t* mask, int64_t n_words, hipStream_t s);
 

@@ -167,21 +167,6 @@ hipError_t launch_fill_mask(uint64_t* mask, int64_t n_words, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Compute units of the current device, asked once per device (every thread
-// that races on the first call stores the same value).
-static int compute_units() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return 256;
-        __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
-    }
-    return n;
-}
-
 hipError_t launch_bank_topk(const float* logits, int64_t T, int d_i, int keep,
                             uint64_t* mask, uint16_t* ids, hipStream_t s, void* const* events,
                             int stage) {

@@ -392,6 +392,27 @@ def test_forward_many_tiles_ragged(full_layer, ffn_full):
     assert torch.equal(y256.view(torch.int16), y[:256].view(torch.int16))
 
 
+@pytest.mark.parametrize("gate,keep", [("silu", 16), ("pred", 40), ("pred", 41)])
+def test_forward_persistent_gate_up(full_layer, gate, keep):
+    """600 tokens: 336 gate/up tiles of 256 x 128, more than the compute
+    units, so with compact gate tiles (keep <= 40) each workgroup walks up to
+    two tiles and requests the next tile's first slab during the epilogue;
+    keep = 41 (full fp16 tiles) runs one tile per workgroup. The last row
+    tile holds 88 tokens. Sampled rows against the oracle, and the first 256
+    rows equal a 256-token call (112 tiles, one per workgroup) bit for bit."""
+    ffn = make_ffn(full_layer, bias=True, keep=keep, gate=gate)
+    T = 600
+    x = wl.make_tokens(wl.FULL, T, seed=3100 + keep, outlier_frac=0.01)
+    xd = dev(x)
+    y, mask, logits = ffn(xd, return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    rows = [0, 255, 256, 300, 511, 512, 599]
+    check_forward(full_layer, x, y, mask, logits, tokens=rows, bias=True, keep=keep, gate=gate)
+    y256 = ffn(xd[:256])
+    torch.cuda.synchronize()
+    assert torch.equal(y256.view(torch.int16), y[:256].view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 5, 64, 200, 300])
 @pytest.mark.parametrize("gate", ["pred", "silu"])
 def test_forward_mid_shapes(mid_layer, T, gate):
