@@ -413,6 +413,24 @@ def test_forward_persistent_gate_up(full_layer, gate, keep):
     assert torch.equal(y256.view(torch.int16), y[:256].view(torch.int16))
 
 
+@pytest.mark.parametrize("d", [64, 576])
+def test_forward_gate_up_k_step_counts(d):
+    """Gate/up over 272 tiles of 256 x 128 (d_i = 2048, 4352 tokens) with a
+    single K step (d = 64: persistent workgroups; the gate tile comes after
+    that step's barrier and the next tile's first slab is requested during
+    the epilogue) and with an odd count of K steps (d = 576: nine, one tile
+    per workgroup). Sampled rows, the last row tile's included, against the
+    oracle."""
+    shape = wl.LayerShape(d=d, d_i=2048, rank=64)
+    layer = wl.make_layer(shape, seed=40 + d, bias_var=0.5)
+    ffn = make_ffn(layer, bias=True)
+    T = 4352
+    x = wl.make_tokens(shape, T, seed=41 + d)
+    y, mask, logits = ffn(dev(x), return_mask=True, return_logits=True)
+    torch.cuda.synchronize()
+    check_forward(layer, x, y, mask, logits, tokens=[0, 255, 256, 2000, 4095, 4096, 4351], bias=True)
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 5, 64, 200, 300])
 @pytest.mark.parametrize("gate", ["pred", "silu"])
 def test_forward_mid_shapes(mid_layer, T, gate):
