@@ -443,6 +443,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(EPI == EPI_
 // of the same 64 channels and 128 tokens.
 // ---------------------------------------------------------------------------
 
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int SLAB = TM * TK * 2;                  // bytes of one operand slab (32 KB)
 
@@ -818,27 +820,34 @@ __global__ __launch_bounds__(128 * WN) void k_gemm256(const GemmParams p, int m_
                         const int ch = tid + i * NT;
                         return reinterpret_cast<const uint4*>(hb + (ch >> 4) * 256 + (ch & 15) * 16);
                     };
+                    // one copy of the element loop per gate, and the drop as a
+                    // select of the value (bf16(0) = 0): no branch per element
+                    auto compute = [&](auto silu) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < NJ / 2; ++j) {
-                            // 16 reads in flight, then the 16 writes
-                            uint16_t* e[16];
-                            uint16_t g[16];
+                            for (int j = 0; j < NJ / 2; ++j) {
+                                // 16 reads in flight, then the 16 writes
+                                uint16_t* e[16];
+                                uint16_t g[16];
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                e[v] = elem(i, j, v);
-                                g[v] = *e[v];
+                                for (int v = 0; v < 16; ++v) {
+                                    e[v] = elem(i, j, v);
+                                    g[v] = *e[v];
+                                }
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) {
+                                    const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
+                                    float sg;
+                                    if constexpr (decltype(silu)::value) sg = sigmoidf_dev(u);
+                                    else sg = (float)__builtin_bit_cast(_Float16, g[v]);
+                                    const bool kept = p.dense || g[v] != kGateDropped;   // dense: no gate tile
+                                    *e[v] = f32_to_bf16(kept ? sg * u * vv : 0.f);
+                                }
                             }
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const float u = acc[i][j][v], vv = acc[i][j + NJ / 2][v];
-                                const float sg =
-                                    p.gate ? sigmoidf_dev(u) : (float)__builtin_bit_cast(_Float16, g[v]);
-                                const bool kept = p.dense || g[v] != kGateDropped;   // dense: no gate tile loaded
-                                *e[v] = kept ? f32_to_bf16(sg * u * vv) : (uint16_t)0;
-                            }
-                        }
+                    };
+                    if (p.gate == kGateSilu) compute(BoolTag<true>{});
+                    else compute(BoolTag<false>{});
                     // this wave's LDS writes done, then the barrier; unlike
                     // __syncthreads it does not wait for the loads still in
                     // flight into the other buffer (the clobber keeps the
