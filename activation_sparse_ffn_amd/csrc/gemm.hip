@@ -7,10 +7,15 @@
 // 3. Hardware Implicaties), with the gate taken from the predictor
 // (Methodologie > 1. Architectuur) and off-mask channels exactly zero.
 //
-//   Z = bf16(X A^T)                 k_gemm<EPI_BF16>
+//   Z = bf16(X A^T)                 k_gemm<EPI_BF16>, or (T >= 256) K-split
+//                                   k_gemm<EPI_PARTIAL> + k_sum_splits_bf16
 //   P = Z B^T + bias (fp32)         k_gemm<EPI_F32_BIAS>
 //   mask = bank top-k of P          k_bank_topk
-//   H = select(m, s * U * V, 0)     k_gemm<EPI_GATEUP>, U = X W_g^T, V = X W_u^T
+//     (T >= 256, d_i % 128 == 0: P, the top-k and the gate tiles in one
+//      kernel, k_gemm<EPI_TOPK>)
+//   H = select(m, s * U * V, 0)     k_gemm<EPI_GATEUP> / k_gemm256<EPI_GATEUP>
+//                                   (persistent with compact gate tiles),
+//                                   U = X W_g^T, V = X W_u^T
 //   Y = bf16(H W_d^T)               k_gemm256 / k_gemm <EPI_BF16, K-major W_d^T>
 //
 // Every GEMM is C[M, N] = A[M, K] B[N, K]^T with A K-contiguous bf16 and
